@@ -1,0 +1,20 @@
+"""Float64 CPU oracle for causal linear attention (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package.  It imports nothing from the HIP library.
+"""
+from .linattn_oracle import (  # noqa: F401
+    ELU1,
+    MAPS,
+    TAYLOR2,
+    attention_quadratic,
+    attention_recurrent,
+    attention_rows,
+    decode_step,
+    feature_dim,
+    feature_map,
+    final_state,
+    kernel_value,
+    phi_elu1,
+    phi_taylor2,
+)

@@ -1,0 +1,198 @@
+"""Float64 CPU oracle for causal linear attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP library
+and imports nothing from it.
+
+Sources (page titles as printed; section in brackets):
+  [TR]  "Transformers are RNNs: Fast Autoregressive Transformers with Linear
+        Attention" -- abstract: attention as a dot product of kernel feature
+        maps, associativity turns O(N^2) into O(N), iterative (RNN) form.
+  [SLA] "Simple linear attention language models balance the
+        recall-throughput tradeoff" -- Knowl 3 (the causal output equation,
+        the recurrent state equations, the Taylor kernel identity) and Knowl 5
+        (prefill writes final states; generation updates the state, then reads
+        it).
+
+Everything here is plain float64 numpy.  The functions follow the
+definitions as written; there is no chunking, blocking or fusion.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  * elu(x)+1 is named by the [TR] abstract's source paper but not defined on
+    the pages: ELU with alpha = 1, so phi(x) = x + 1 for x > 0 and exp(x) for
+    x <= 0 (both branches give 1 at 0).
+  * The Taylor map is [1, x, vec(x outer x)/sqrt(2)] with vec in row-major
+    order, feature index 1 + d + i*d + j for x_i*x_j; [SLA] Knowl 3 gives only
+    the identity phi(q).phi(k) = 1 + q.k + (q.k)^2/2 and "constant,
+    first-order, second-order pairwise products".
+  * The causal sum includes the diagonal (sum over j = 1..i, [SLA] Knowl 3).
+  * No epsilon in the denominator; it is positive for both maps.
+  * Generation updates the state first and then reads it ([SLA] Knowl 3
+    recurrent equations; Knowl 5 second paragraph).
+
+Parity pins (all in tests/test_oracle_pins.py): exact rational brute force,
+quadratic == recurrent, Taylor identity and its exp limit, torch's elu,
+closed-form special cases (first token, constant key, zero Taylor query,
+constant value), convex-hull and positivity invariants, final-state closed
+form, decode continuation, and a hand-worked golden example.  Every function
+below is pinned; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ELU1 = "elu1"
+TAYLOR2 = "taylor2"
+MAPS = (ELU1, TAYLOR2)
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Feature maps
+# --------------------------------------------------------------------------
+def phi_elu1(x) -> np.ndarray:
+    """elu(x) + 1 elementwise, ELU with alpha = 1 (reading; see header)."""
+    x = _f64(x)
+    return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def phi_taylor2(x) -> np.ndarray:
+    """Second-order Taylor map [1, x, vec(x (x) x)/sqrt(2)] over the last axis.
+
+    [SLA] Knowl 3: the map is the concatenation of a constant term, the
+    first-order coordinates and the second-order pairwise products, chosen so
+    that phi(q).phi(k) = 1 + q.k + (q.k)^2/2.  Output width 1 + d + d*d.
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    ones = np.ones(x.shape[:-1] + (1,), dtype=np.float64)
+    outer = x[..., :, None] * x[..., None, :]             # [..., d, d], (i, j)
+    quad = outer.reshape(x.shape[:-1] + (d * d,)) / math.sqrt(2.0)
+    return np.concatenate([ones, x, quad], axis=-1)
+
+
+def feature_dim(fmap: str, d_k: int) -> int:
+    if fmap == ELU1:
+        return d_k
+    if fmap == TAYLOR2:
+        return 1 + d_k + d_k * d_k
+    raise ValueError(f"unknown feature map {fmap!r}")
+
+
+def feature_map(x, fmap: str) -> np.ndarray:
+    if fmap == ELU1:
+        return phi_elu1(x)
+    if fmap == TAYLOR2:
+        return phi_taylor2(x)
+    raise ValueError(f"unknown feature map {fmap!r}")
+
+
+# --------------------------------------------------------------------------
+# The causal output: definition (quadratic masked form)
+# --------------------------------------------------------------------------
+def attention_quadratic(q, k, v, fmap: str) -> np.ndarray:
+    """y_i = phi(q_i) sum_{j<=i} phi(k_j)^T v_j / phi(q_i) sum_{j<=i} phi(k_j)^T.
+
+    [SLA] Knowl 3, first equation, written as ((phi(Q) phi(K)^T) * M) V divided
+    row by row by ((phi(Q) phi(K)^T) * M) 1, with M lower-triangular including
+    the diagonal.  q, k: [..., N, d_k]; v: [..., N, d_v].  O(N^2) memory: for
+    small N only (see attention_rows for single rows at any N).
+    """
+    fq = feature_map(q, fmap)
+    fk = feature_map(k, fmap)
+    v = _f64(v)
+    n = fq.shape[-2]
+    scores = fq @ np.swapaxes(fk, -1, -2)                   # [..., N, N]
+    mask = np.tril(np.ones((n, n), dtype=np.float64))
+    w = scores * mask
+    num = w @ v
+    den = w.sum(axis=-1)
+    return num / den[..., None]
+
+
+def attention_rows(q, k, v, fmap: str, rows) -> np.ndarray:
+    """The same definition evaluated only at the (0-based) positions `rows`.
+
+    q, k: [N, d_k], v: [N, d_v] for ONE sequence and head.  Each output row
+    t needs phi(q_t) and phi(k_1..k_t): O(t * (D + d_v)) work, so it can be
+    used at any sequence length.  Returns [len(rows), d_v].
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    out = np.empty((len(rows), v.shape[-1]), dtype=np.float64)
+    for r, t in enumerate(rows):
+        fq = feature_map(q[t], fmap)                        # [D]
+        fk = feature_map(k[: t + 1], fmap)                  # [t+1, D]
+        w = fk @ fq                                         # [t+1]
+        out[r] = (w @ v[: t + 1]) / w.sum()
+    return out
+
+
+# --------------------------------------------------------------------------
+# Recurrent form
+# --------------------------------------------------------------------------
+def decode_step(q, k, v, S, z, fmap: str):
+    """One recurrent step from the state (S, z); returns (y, S_new, z_new).
+
+    [SLA] Knowl 3 second equation: s_i = s_{i-1} + phi(k_i)^T v_i,
+    z_i = z_{i-1} + phi(k_i)^T, y_i = phi(q_i) s_i / phi(q_i) z_i -- the state
+    is updated before it is read (Knowl 5, generation paragraph).
+    q, k: [..., d_k]; v: [..., d_v]; S: [..., D, d_v]; z: [..., D].
+    The inputs are not modified.
+    """
+    fq = feature_map(q, fmap)
+    fk = feature_map(k, fmap)
+    v = _f64(v)
+    S_new = _f64(S) + fk[..., :, None] * v[..., None, :]
+    z_new = _f64(z) + fk
+    num = np.einsum("...r,...rc->...c", fq, S_new)
+    den = np.einsum("...r,...r->...", fq, z_new)
+    return num / den[..., None], S_new, z_new
+
+
+def attention_recurrent(q, k, v, fmap: str, S0=None, z0=None):
+    """Run the recurrence over all N positions; returns (y, S_N, z_N).
+
+    q, k: [..., N, d_k]; v: [..., N, d_v].  The state starts at zero (the sums
+    of the definition start at j = 1) unless (S0, z0) is given, in which case
+    the sequence continues from that state.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    batch = q.shape[:-2]
+    n = q.shape[-2]
+    D = feature_dim(fmap, q.shape[-1])
+    dv = v.shape[-1]
+    S = np.zeros(batch + (D, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros(batch + (D,)) if z0 is None else _f64(z0).copy()
+    y = np.empty(batch + (n, dv), dtype=np.float64)
+    for t in range(n):
+        y[..., t, :], S, z = decode_step(q[..., t, :], k[..., t, :],
+                                         v[..., t, :], S, z, fmap)
+    return y, S, z
+
+
+def final_state(k, v, fmap: str):
+    """Closed form of the state after N tokens: S_N = phi(K)^T V, z_N = phi(K)^T 1.
+
+    [SLA] Knowl 3 (the recurrence summed) and Knowl 5 (prefill optionally
+    writes the final states for later generation).
+    """
+    fk = feature_map(k, fmap)
+    v = _f64(v)
+    S = np.swapaxes(fk, -1, -2) @ v
+    z = fk.sum(axis=-2)
+    return S, z
+
+
+def kernel_value(q, k, fmap: str) -> np.ndarray:
+    """phi(q) . phi(k) over the last axis, through the explicit features."""
+    return np.sum(feature_map(q, fmap) * feature_map(k, fmap), axis=-1)
