@@ -1,0 +1,323 @@
+// C ABI of the library: argument validation, segment planning and dispatch
+// to the kernel instantiations.  Declared in include/linattn.h.
+//
+// Everything here runs on the host.  Validation finishes before the first
+// HIP call, so an invalid call neither launches nor writes anything and
+// makes no HIP runtime call at all.
+#include <limits.h>
+#include <stdint.h>
+
+#include "linattn.h"
+#include "shapes.hpp"
+
+namespace linattn {
+typedef uint16_t bf16_t;
+}
+
+namespace {
+
+using namespace linattn;
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kChunk = 64;     // tokens per chunk inside the prefill kernels
+constexpr int kTargetWorkgroups = 256;  // MI355X compute units
+constexpr int64_t kMinSegChunks = 8;    // shortest default segment (chunks)
+constexpr int64_t kMaxElems = (int64_t)1 << 46;
+
+#define LINATTN_FOR_SHAPES(X)                                                 \
+  X(MAP_ELU1, 16, 16)                                                         \
+  X(MAP_ELU1, 32, 32)                                                         \
+  X(MAP_ELU1, 64, 64)                                                         \
+  X(MAP_TAYLOR2, 16, 16)                                                      \
+  X(MAP_TAYLOR2, 16, 32)                                                      \
+  X(MAP_TAYLOR2, 16, 64)
+
+bool valid_map(int map) {
+  return map == LINATTN_MAP_ELU1 || map == LINATTN_MAP_TAYLOR2;
+}
+
+bool valid_dtype(int dtype) {
+  return dtype == LINATTN_DTYPE_F32 || dtype == LINATTN_DTYPE_BF16;
+}
+
+bool is_supported(int map, int dtype, int64_t dk, int64_t dv) {
+  if (!valid_map(map) || !valid_dtype(dtype)) return false;
+#define X(M, DK, DV) \
+  if (map == M && dk == DK && dv == DV) return true;
+  LINATTN_FOR_SHAPES(X)
+#undef X
+  return false;
+}
+
+int64_t feature_dim(int map, int64_t dk) {
+  if (dk <= 0 || dk > (1 << 20)) return -1;
+  if (map == LINATTN_MAP_ELU1) return dk;
+  if (map == LINATTN_MAP_TAYLOR2) return 1 + dk + dk * dk;
+  return -1;
+}
+
+int64_t slot_floats(int map, int64_t dk, int64_t dv) {
+#define X(M, DK, DV) \
+  if (map == M && dk == DK && dv == DV) return StateShape<M, DK, DV>::SLOT;
+  LINATTN_FOR_SHAPES(X)
+#undef X
+  return -1;
+}
+
+size_t elem_size(int dtype) { return dtype == LINATTN_DTYPE_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+struct Range {
+  const char* p;
+  size_t n;
+};
+
+bool overlap(Range a, Range b) {
+  if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+  return a.p < b.p + b.n && b.p < a.p + a.n;
+}
+
+Range rng(const void* p, int64_t elems, size_t esz) {
+  return Range{reinterpret_cast<const char*>(p), (size_t)elems * esz};
+}
+
+// Segments along N: each workgroup walks seg_chunks consecutive chunks.
+bool plan_segments(int64_t BH, int64_t N, int64_t seg_len, int* nseg_out,
+                   int* seg_chunks_out) {
+  const int64_t nchunks = (N + kChunk - 1) / kChunk;
+  int64_t seg_chunks;
+  if (seg_len == 0) {
+    int64_t nseg = (kTargetWorkgroups + BH - 1) / BH;
+    int64_t max_nseg = nchunks / kMinSegChunks;
+    if (max_nseg < 1) max_nseg = 1;
+    if (nseg > max_nseg) nseg = max_nseg;
+    if (nseg < 1) nseg = 1;
+    seg_chunks = (nchunks + nseg - 1) / nseg;
+  } else {
+    if (seg_len < 0 || seg_len % kChunk != 0) return false;
+    seg_chunks = seg_len / kChunk;
+  }
+  if (seg_chunks > nchunks) seg_chunks = nchunks;
+  const int64_t nseg = (nchunks + seg_chunks - 1) / seg_chunks;
+  if (BH * nseg > INT_MAX || seg_chunks > INT_MAX) return false;
+  *nseg_out = (int)nseg;
+  *seg_chunks_out = (int)seg_chunks;
+  return true;
+}
+
+size_t workspace_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nseg) {
+  if (nseg <= 1) return 0;
+  return (size_t)BH * (size_t)nseg * (size_t)slot_floats(map, dk, dv) * 4u;
+}
+
+hipError_t dispatch_prefill(int map, int dtype, int64_t dk, int64_t dv,
+                            const PrefillArgs& a, hipStream_t st) {
+#define X(M, DK, DV)                                                     \
+  if (map == M && dk == DK && dv == DV)                                  \
+    return dtype == LINATTN_DTYPE_F32 ? launch_prefill<M, float, DK, DV>(a, st) \
+                                      : launch_prefill<M, bf16_t, DK, DV>(a, st);
+  LINATTN_FOR_SHAPES(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_decode(int map, int dtype, int64_t dk, int64_t dv,
+                           const void* q, const void* k, const void* v,
+                           float* S, float* z, void* y, int64_t BH,
+                           hipStream_t st) {
+#define X(M, DK, DV)                                                            \
+  if (map == M && dk == DK && dv == DV)                                         \
+    return dtype == LINATTN_DTYPE_F32                                           \
+               ? launch_decode<M, float, DK, DV>(q, k, v, S, z, y, BH, st)      \
+               : launch_decode<M, bf16_t, DK, DV>(q, k, v, S, z, y, BH, st);
+  LINATTN_FOR_SHAPES(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* linattn_status_string(int status) {
+  switch (status) {
+    case LINATTN_OK:
+      return "ok";
+    case LINATTN_ERR_INVALID_ARGUMENT:
+      return "invalid argument (null pointer, non-positive size, misaligned or overlapping buffer, bad segment length)";
+    case LINATTN_ERR_UNSUPPORTED:
+      return "unsupported combination of feature map, dtype, d_k and d_v";
+    case LINATTN_ERR_WORKSPACE:
+      return "workspace missing or smaller than linattn_prefill_workspace_bytes()";
+    case LINATTN_ERR_HIP:
+      return "the HIP runtime reported an error while launching";
+    default:
+      return "unknown status";
+  }
+}
+
+int linattn_version(void) { return kVersion; }
+
+int64_t linattn_feature_dim(int map, int64_t d_k) { return feature_dim(map, d_k); }
+
+int linattn_supported(int map, int dtype, int64_t d_k, int64_t d_v) {
+  return is_supported(map, dtype, d_k, d_v) ? 1 : 0;
+}
+
+linattn_status_t linattn_feature_map(int map, int dtype, const void* x,
+                                     int64_t rows, int64_t d_k, float* phi,
+                                     void* stream) {
+  if (!valid_map(map) || !valid_dtype(dtype) || rows < 0 || d_k <= 0)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  const bool ok_dk = map == LINATTN_MAP_ELU1 ? (d_k == 16 || d_k == 32 || d_k == 64)
+                                             : d_k == 16;
+  if (!ok_dk) return LINATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return LINATTN_OK;
+  const int64_t D = feature_dim(map, d_k);
+  if (rows > kMaxElems / D) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (x == nullptr || phi == nullptr || !aligned16(x) || !aligned16(phi))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (overlap(rng(x, rows * d_k, elem_size(dtype)), rng(phi, rows * D, 4)))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (map == LINATTN_MAP_ELU1)
+    e = dtype == LINATTN_DTYPE_F32
+            ? launch_feature_map<MAP_ELU1, float>(x, rows, (int)d_k, phi, st)
+            : launch_feature_map<MAP_ELU1, bf16_t>(x, rows, (int)d_k, phi, st);
+  else
+    e = dtype == LINATTN_DTYPE_F32
+            ? launch_feature_map<MAP_TAYLOR2, float>(x, rows, (int)d_k, phi, st)
+            : launch_feature_map<MAP_TAYLOR2, bf16_t>(x, rows, (int)d_k, phi, st);
+  return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
+size_t linattn_prefill_workspace_bytes(int map, int dtype, int64_t B, int64_t H,
+                                       int64_t N, int64_t d_k, int64_t d_v,
+                                       int64_t seg_len) {
+  if (!valid_map(map) || !valid_dtype(dtype) || B <= 0 || H <= 0 || N <= 0 ||
+      d_k <= 0 || d_v <= 0)
+    return (size_t)-1;
+  if (!is_supported(map, dtype, d_k, d_v)) return (size_t)-1;
+  if (B > kMaxElems / H || N > kMaxElems / (B * H)) return (size_t)-1;
+  int nseg, seg_chunks;
+  if (!plan_segments(B * H, N, seg_len, &nseg, &seg_chunks)) return (size_t)-1;
+  return workspace_bytes(map, B * H, d_k, d_v, nseg);
+}
+
+linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,
+                                 int64_t N, int64_t d_k, int64_t d_v,
+                                 const void* q, const void* k, const void* v,
+                                 void* y, const float* S_in, const float* z_in,
+                                 float* S_out, float* z_out, int64_t seg_len,
+                                 void* workspace, size_t workspace_bytes_given,
+                                 void* stream) {
+  if (!valid_map(map) || !valid_dtype(dtype) || B <= 0 || H <= 0 || N <= 0 ||
+      d_k <= 0 || d_v <= 0)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!is_supported(map, dtype, d_k, d_v)) return LINATTN_ERR_UNSUPPORTED;
+  if (B > kMaxElems / H || N > kMaxElems / (B * H * (d_k > d_v ? d_k : d_v)))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  const int64_t BH = B * H;
+  if (BH > INT_MAX) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (q == nullptr || k == nullptr || v == nullptr || y == nullptr)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if ((S_in && (!aligned4(S_in) || !aligned4(z_in))) ||
+      (S_out && (!aligned4(S_out) || !aligned4(z_out))))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  int nseg, seg_chunks;
+  if (!plan_segments(BH, N, seg_len, &nseg, &seg_chunks))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+
+  const size_t es = elem_size(dtype);
+  const int64_t D = feature_dim(map, d_k);
+  const Range rq = rng(q, BH * N * d_k, es), rk = rng(k, BH * N * d_k, es);
+  const Range rv = rng(v, BH * N * d_v, es), ry = rng(y, BH * N * d_v, es);
+  const Range rSi = rng(S_in, BH * D * d_v, 4), rzi = rng(z_in, BH * D, 4);
+  const Range rSo = rng(S_out, BH * D * d_v, 4), rzo = rng(z_out, BH * D, 4);
+  // outputs must not overlap inputs or each other (S_out == S_in and
+  // z_out == z_in exactly are allowed: in-place continuation)
+  const Range outs[3] = {ry, rSo, rzo};
+  const Range ins[3] = {rq, rk, rv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(outs[i], ins[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+  }
+  if (overlap(ry, rSi) || overlap(ry, rzi)) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (overlap(rSo, rSi) && S_out != S_in) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (overlap(rzo, rzi) && z_out != z_in) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (overlap(rSo, rzi) || overlap(rzo, rSi)) return LINATTN_ERR_INVALID_ARGUMENT;
+
+  const size_t need = workspace_bytes(map, BH, d_k, d_v, nseg);
+  if (need > 0) {
+    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes_given < need)
+      return LINATTN_ERR_WORKSPACE;
+    const Range rw{reinterpret_cast<const char*>(workspace), need};
+    const Range all[8] = {rq, rk, rv, ry, rSi, rzi, rSo, rzo};
+    for (int i = 0; i < 8; ++i)
+      if (overlap(rw, all[i])) return LINATTN_ERR_INVALID_ARGUMENT;
+  }
+
+  PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.y = y;
+  a.S_in = S_in;
+  a.z_in = z_in;
+  a.S_out = S_out;
+  a.z_out = z_out;
+  a.ws = reinterpret_cast<float*>(workspace);
+  a.N = N;
+  a.BH = (int)BH;
+  a.nseg = nseg;
+  a.seg_chunks = seg_chunks;
+  const hipError_t e =
+      dispatch_prefill(map, dtype, d_k, d_v, a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
+linattn_status_t linattn_decode_step(int map, int dtype, int64_t B, int64_t H,
+                                     int64_t d_k, int64_t d_v, const void* q,
+                                     const void* k, const void* v, float* S,
+                                     float* z, void* y, void* stream) {
+  if (!valid_map(map) || !valid_dtype(dtype) || B <= 0 || H <= 0 || d_k <= 0 ||
+      d_v <= 0)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!is_supported(map, dtype, d_k, d_v)) return LINATTN_ERR_UNSUPPORTED;
+  if (B > kMaxElems / H) return LINATTN_ERR_INVALID_ARGUMENT;
+  const int64_t BH = B * H;
+  if (BH > INT_MAX) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (q == nullptr || k == nullptr || v == nullptr || S == nullptr || z == nullptr ||
+      y == nullptr)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) ||
+      !aligned16(z) || !aligned16(y))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  const size_t es = elem_size(dtype);
+  const int64_t D = feature_dim(map, d_k);
+  const Range rq = rng(q, BH * d_k, es), rk = rng(k, BH * d_k, es);
+  const Range rv = rng(v, BH * d_v, es), ry = rng(y, BH * d_v, es);
+  const Range rS = rng(S, BH * D * d_v, 4), rz = rng(z, BH * D, 4);
+  const Range ins[3] = {rq, rk, rv};
+  const Range outs[3] = {ry, rS, rz};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(outs[i], ins[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = dispatch_decode(map, dtype, d_k, d_v, q, k, v, S, z, y, BH,
+                                       reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
+}  // extern "C"

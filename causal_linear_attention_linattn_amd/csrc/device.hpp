@@ -1,0 +1,184 @@
+// Device-side building blocks shared by the gfx950 kernels: element types,
+// bf16 rounding, MFMA fragments and the two feature maps.
+//
+// Feature maps ("Simple linear attention language models balance the
+// recall-throughput tradeoff", Knowl 3):
+//   ELU1    phi(x) = elu(x) + 1 = x + 1 (x > 0), exp(x) (x <= 0).
+//   TAYLOR2 phi(x) = [1, x, vec(x (x) x)/sqrt 2], so phi(q).phi(k) =
+//           1 + q.k + (q.k)^2 / 2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "shapes.hpp"
+
+namespace linattn {
+
+typedef uint16_t bf16_t;  // bf16 storage: raw bit pattern
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr float kInvSqrt2 = 0.70710678118654752440f;
+constexpr float kSqrt2 = 1.41421356237309504880f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// Workgroup barrier that orders LDS traffic only.  __syncthreads() would
+// also wait for every outstanding global load of the calling wave, which
+// would drain the prefetch of the next tile before each barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ float phi_elu1(float x) {
+  return x > 0.0f ? x + 1.0f : __expf(x);
+}
+
+// ---------------------------------------------------------------------------
+// Element traits: T is the storage type of q, k, v, y (float or bf16_t).
+// A "fragment" is one lane's 8-element share of an MFMA operand: for
+// v_mfma_f32_16x16x32_bf16 the 64 lanes hold a 16 x 32 operand, lane l
+// owning row (l % 16) and eight K slots of lane group (l / 16).  The float32
+// path emulates the same 16x16x32 step with eight v_mfma_f32_16x16x4_f32.
+// Which logical K index a (lane group, slot) pair stands for is up to the
+// caller; the product is correct whenever A and B use the same assignment.
+// ---------------------------------------------------------------------------
+template <typename T> struct Elem;
+
+template <> struct Elem<bf16_t> {
+  typedef bf16x8_t frag;
+  static constexpr int kPer16B = 8;  // elements per 16-byte vector
+  __device__ static __forceinline__ float to_f32(bf16_t x) {
+    return bf16_to_f32(x);
+  }
+  __device__ static __forceinline__ bf16_t from_f32(float x) {
+    return f32_to_bf16(x);
+  }
+  __device__ static __forceinline__ frag make(const float (&v)[8]) {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (__bf16)v[i];
+    return f;
+  }
+  __device__ static __forceinline__ frag zero() {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (__bf16)0.0f;
+    return f;
+  }
+  // 8 consecutive elements, 16-byte aligned (LDS or global).
+  __device__ static __forceinline__ frag load8(const bf16_t* p) {
+    return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(p));
+  }
+  __device__ static __forceinline__ void load8f(const bf16_t* p, float (&v)[8]) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static __forceinline__ void mma(f32x4_t& acc, const frag& a,
+                                             const frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+};
+
+template <> struct Elem<float> {
+  typedef f32x8_t frag;
+  static constexpr int kPer16B = 4;
+  __device__ static __forceinline__ float to_f32(float x) { return x; }
+  __device__ static __forceinline__ float from_f32(float x) { return x; }
+  __device__ static __forceinline__ frag make(const float (&v)[8]) {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = v[i];
+    return f;
+  }
+  __device__ static __forceinline__ frag zero() {
+    frag f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+    return f;
+  }
+  __device__ static __forceinline__ frag load8(const float* p) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    frag f;
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    return f;
+  }
+  __device__ static __forceinline__ void load8f(const float* p, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ static __forceinline__ void mma(f32x4_t& acc, const frag& a,
+                                             const frag& b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+  }
+};
+
+// Unpack one 16-byte vector of stored elements into floats.
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& u,
+                                         float (&v)[Elem<T>::kPer16B]);
+
+template <>
+__device__ __forceinline__ void unpack16<bf16_t>(const uint4& u,
+                                                 float (&v)[8]) {
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& u,
+                                                float (&v)[4]) {
+  v[0] = __uint_as_float(u.x);
+  v[1] = __uint_as_float(u.y);
+  v[2] = __uint_as_float(u.z);
+  v[3] = __uint_as_float(u.w);
+}
+
+// Pack floats into one 16-byte vector of stored elements.
+template <typename T>
+__device__ __forceinline__ uint4 pack16(const float (&v)[Elem<T>::kPer16B]);
+
+template <>
+__device__ __forceinline__ uint4 pack16<bf16_t>(const float (&v)[8]) {
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                    pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
+template <>
+__device__ __forceinline__ uint4 pack16<float>(const float (&v)[4]) {
+  return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
+                    __float_as_uint(v[2]), __float_as_uint(v[3]));
+}
+
+}  // namespace linattn

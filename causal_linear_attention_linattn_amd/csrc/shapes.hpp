@@ -1,0 +1,53 @@
+// Shapes and launch arguments shared by the host API and the prefill
+// kernels (no kernel code here).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace linattn {
+
+enum { MAP_ELU1 = 0, MAP_TAYLOR2 = 1 };
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* y;
+  const float* S_in;
+  const float* z_in;
+  float* S_out;
+  float* z_out;
+  float* ws;
+  int64_t N;
+  int BH;
+  int nseg;        // segments per (batch, head)
+  int seg_chunks;  // chunks per segment
+};
+
+template <int MAP, int DK, int DV>
+struct StateShape {
+  static constexpr int D = MAP == MAP_ELU1 ? DK : 1 + DK + DK * DK;
+  static constexpr int DP = MAP == MAP_ELU1 ? ((DK + 31) / 32) * 32 : 288;
+  static constexpr int NRT = DP / 16;    // 16-row tiles of S'
+  static constexpr int NKB = DP / 32;    // 32-wide K blocks over features
+  static constexpr int NCT = DV / 16 + 1;  // column tiles of S' incl. z
+  static constexpr int NCOL = 16 * NCT;
+  static constexpr int SLOT = NRT * NCT * 256;  // floats per workspace slot
+  static_assert(MAP == MAP_ELU1 || DK == 16, "TAYLOR2 is built for d_k = 16");
+  static_assert(DK % 16 == 0 && DV % 16 == 0, "d_k, d_v multiples of 16");
+};
+
+template <int MAP, typename T, int DK, int DV>
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+
+template <int MAP, typename T, int DK, int DV>
+hipError_t launch_decode(const void* q, const void* k, const void* v,
+                         float* S, float* z, void* y, int64_t BH,
+                         hipStream_t st);
+
+template <int MAP, typename T>
+hipError_t launch_feature_map(const void* x, int64_t rows, int d_k,
+                              float* phi, hipStream_t st);
+
+}  // namespace linattn

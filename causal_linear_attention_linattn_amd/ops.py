@@ -1,0 +1,215 @@
+"""Python binding of liblinattn.so: argument marshalling only.
+
+Every step of the computation runs in the HIP library.  PyTorch supplies
+device memory and the current HIP stream; nothing here computes on the
+data.  If the library is missing the first call raises ImportError -- there
+is no fallback path.
+
+Entry points (same names as the C ABI in include/linattn.h):
+    feature_map(x, fmap)                      -> phi(x) float32 [..., D]
+    prefill(q, k, v, fmap, state=None, ...)   -> y (and the final state)
+    decode_step(q, k, v, S, z, fmap)          -> y; S, z updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "liblinattn.so")
+
+MAPS = {"elu1": 0, "taylor2": 1}
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace",
+           4: "hip error"}
+
+_lib = None
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"linattn status {status}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and return the library; raises ImportError if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run "
+            "`python -m causal_linear_attention_linattn_amd._build`")
+    L = ctypes.CDLL(path)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    fp = ctypes.c_void_p
+    L.linattn_status_string.argtypes = [i32]
+    L.linattn_status_string.restype = ctypes.c_char_p
+    L.linattn_version.argtypes = []
+    L.linattn_version.restype = i32
+    L.linattn_feature_dim.argtypes = [i32, i64]
+    L.linattn_feature_dim.restype = i64
+    L.linattn_supported.argtypes = [i32, i32, i64, i64]
+    L.linattn_supported.restype = i32
+    L.linattn_feature_map.argtypes = [i32, i32, vp, i64, i64, fp, vp]
+    L.linattn_feature_map.restype = i32
+    L.linattn_prefill_workspace_bytes.argtypes = [i32, i32, i64, i64, i64, i64,
+                                                  i64, i64]
+    L.linattn_prefill_workspace_bytes.restype = sz
+    L.linattn_prefill.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp,
+                                  vp, fp, fp, fp, fp, i64, vp, sz, vp]
+    L.linattn_prefill.restype = i32
+    L.linattn_decode_step.argtypes = [i32, i32, i64, i64, i64, i64, vp, vp, vp,
+                                      fp, fp, vp, vp]
+    L.linattn_decode_step.restype = i32
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().linattn_status_string(status).decode()
+        raise LinAttnError(status, msg)
+
+
+def _map_id(fmap: str) -> int:
+    try:
+        return MAPS[fmap]
+    except KeyError:
+        raise ValueError(f"unknown feature map {fmap!r}; expected one of "
+                         f"{sorted(MAPS)}") from None
+
+
+def _dtype_id(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"dtype {t.dtype} is not supported (float32, bfloat16)") from None
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("linattn tensors must live on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError("linattn tensors must be contiguous")
+
+
+def feature_dim(fmap: str, d_k: int) -> int:
+    return int(load_library().linattn_feature_dim(_map_id(fmap), d_k))
+
+
+def supported(fmap: str, dtype: torch.dtype, d_k: int, d_v: int) -> bool:
+    return bool(load_library().linattn_supported(_map_id(fmap), _DTYPES[dtype],
+                                                 d_k, d_v))
+
+
+def workspace_bytes(fmap, dtype, B, H, N, d_k, d_v, seg_len=0) -> int:
+    n = load_library().linattn_prefill_workspace_bytes(
+        _map_id(fmap), _DTYPES[dtype], B, H, N, d_k, d_v, seg_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise LinAttnError(1, "invalid or unsupported prefill shape")
+    return int(n)
+
+
+def feature_map(x: torch.Tensor, fmap: str) -> torch.Tensor:
+    """phi(x) over the last axis, float32 [..., D] (test/inspection export)."""
+    L = load_library()
+    _need_cuda(x)
+    d_k = x.shape[-1]
+    D = feature_dim(fmap, d_k)
+    rows = x.numel() // d_k if d_k else 0
+    out = torch.empty(x.shape[:-1] + (D,), dtype=torch.float32, device=x.device)
+    _check(L.linattn_feature_map(_map_id(fmap), _dtype_id(x), _ptr(x), rows,
+                                 d_k, _ptr(out), _stream(x)))
+    return out
+
+
+def prefill(q, k, v, fmap: str, *, state=None, return_state=False,
+            seg_len: int = 0, out=None):
+    """Causal linear attention over [B, H, N, d] inputs.
+
+    state: optional (S, z) float32 tensors [B,H,D,d_v], [B,H,D] to continue
+    from.  return_state: also return the final (S, z).  seg_len: tokens per
+    workgroup segment (0 = library choice, else a multiple of 64).
+    """
+    L = load_library()
+    _need_cuda(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("expected q, k [B,H,N,d_k] and v [B,H,N,d_v]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, H, N, d_k = q.shape
+    d_v = v.shape[-1]
+    D = feature_dim(fmap, d_k)
+    y = out if out is not None else torch.empty_like(v)
+    _need_cuda(y)
+    S_in = z_in = None
+    if state is not None:
+        S_in, z_in = state
+        _need_cuda(S_in, z_in)
+        if S_in.dtype != torch.float32 or z_in.dtype != torch.float32:
+            raise TypeError("state tensors must be float32")
+        if tuple(S_in.shape) != (B, H, D, d_v) or tuple(z_in.shape) != (B, H, D):
+            raise ValueError("state shapes must be [B,H,D,d_v] and [B,H,D]")
+    S_out = z_out = None
+    if return_state:
+        S_out = torch.empty((B, H, D, d_v), dtype=torch.float32, device=q.device)
+        z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    nws = workspace_bytes(fmap, q.dtype, B, H, N, d_k, d_v, seg_len)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
+    _check(L.linattn_prefill(_map_id(fmap), _dtype_id(q), B, H, N, d_k, d_v,
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(S_in),
+                             _ptr(z_in), _ptr(S_out), _ptr(z_out), seg_len,
+                             _ptr(ws), nws, _stream(q)))
+    if return_state:
+        return y, (S_out, z_out)
+    return y
+
+
+def decode_step(q, k, v, S, z, fmap: str, *, out=None):
+    """One generation step; q, k [B,H,d_k], v [B,H,d_v].  S, z updated in place."""
+    L = load_library()
+    _need_cuda(q, k, v, S, z)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q, k [B,H,d_k] and v [B,H,d_v]")
+    B, H, d_k = q.shape
+    d_v = v.shape[-1]
+    D = feature_dim(fmap, d_k)
+    if S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise TypeError("state tensors must be float32")
+    if tuple(S.shape) != (B, H, D, d_v) or tuple(z.shape) != (B, H, D):
+        raise ValueError("state shapes must be [B,H,D,d_v] and [B,H,D]")
+    y = out if out is not None else torch.empty_like(v)
+    _check(L.linattn_decode_step(_map_id(fmap), _dtype_id(q), B, H, d_k, d_v,
+                                 _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
+                                 _ptr(y), _stream(q)))
+    return y
+
+
+# ---------------------------------------------------------------- helpers --
+def to_device(stored, device) -> torch.Tensor:
+    """A synth.Stored array (float32 or bf16 bits) as a device tensor."""
+    if stored.dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(stored.data)).to(device)
+    bits = np.ascontiguousarray(stored.data).view(np.int16)
+    return torch.from_numpy(bits).view(torch.bfloat16).to(device)
+
+
+def to_numpy64(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> float64 numpy (exact widening of its values)."""
+    return t.detach().to("cpu", torch.float32).double().numpy()

@@ -1,0 +1,159 @@
+/*
+ * linattn.h -- C ABI of the causal linear-attention library for AMD Instinct
+ * MI355X (gfx950).  Plain C: pointers, sizes and integer codes only.
+ *
+ * The method.  Attention is the dot product of kernel feature maps phi
+ * ("Transformers are RNNs: Fast Autoregressive Transformers with Linear
+ * Attention", abstract).  For causal inputs the output at position i is
+ *     y_i = phi(q_i) (sum_{j<=i} phi(k_j)^T v_j) / phi(q_i) (sum_{j<=i} phi(k_j)^T)
+ * and the sums are carried as a value state S (D x d_v) and a key state z (D):
+ *     S_i = S_{i-1} + phi(k_i)^T v_i,  z_i = z_{i-1} + phi(k_i)^T,
+ *     y_i = phi(q_i) S_i / phi(q_i) z_i
+ * ("Simple linear attention language models balance the recall-throughput
+ * tradeoff", Knowl 3, both equations).
+ *
+ * Feature maps (linattn_map_t):
+ *   LINATTN_MAP_ELU1    phi(x) = elu(x) + 1 elementwise, alpha = 1; D = d_k.
+ *   LINATTN_MAP_TAYLOR2 phi(x) = [1, x, vec(x (x) x)/sqrt(2)], row-major vec
+ *                       (feature 1 + d_k + a*d_k + b is x_a x_b / sqrt 2);
+ *                       D = 1 + d_k + d_k^2, so phi(q).phi(k) = 1 + q.k +
+ *                       (q.k)^2/2 (same page, Knowl 3).
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library allocates and frees nothing and keeps no global state.
+ *   - Tensors are contiguous, row-major, and their base address is 16-byte
+ *     aligned.  q, k, v, y share one element type (linattn_dtype_t); the
+ *     states S, z are always float32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work and return; they never synchronise the host.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     a non-zero status nothing has been enqueued and nothing written.  A
+ *     launch failure reported by the HIP runtime returns LINATTN_ERR_HIP.
+ *   - Outputs must not overlap inputs, except where a call says otherwise.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics).
+ *   - Supported shapes (anything else returns LINATTN_ERR_UNSUPPORTED):
+ *       ELU1:    d_k == d_v in {16, 32, 64}
+ *       TAYLOR2: d_k == 16, d_v in {16, 32, 64}   (D = 273)
+ *     for both dtypes, any B, H >= 1 and any N >= 1 (ragged tails are
+ *     masked inside the kernels).
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum linattn_status {
+  LINATTN_OK = 0,
+  LINATTN_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, size <= 0, misaligned */
+  LINATTN_ERR_UNSUPPORTED = 2,      /* valid but not built: map/dtype/d_k/d_v */
+  LINATTN_ERR_WORKSPACE = 3,        /* workspace missing or too small */
+  LINATTN_ERR_HIP = 4               /* the HIP runtime rejected a launch */
+} linattn_status_t;
+
+typedef enum linattn_map {
+  LINATTN_MAP_ELU1 = 0,
+  LINATTN_MAP_TAYLOR2 = 1
+} linattn_map_t;
+
+typedef enum linattn_dtype {
+  LINATTN_DTYPE_F32 = 0,
+  LINATTN_DTYPE_BF16 = 1
+} linattn_dtype_t;
+
+/* Static text for a status code (never NULL). */
+const char* linattn_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int linattn_version(void);
+
+/* Feature dimension D of a map: ELU1 -> d_k; TAYLOR2 -> 1 + d_k + d_k^2.
+   Returns -1 for an unknown map or d_k <= 0. */
+int64_t linattn_feature_dim(int map, int64_t d_k);
+
+/* 1 if (map, dtype, d_k, d_v) is one of the built kernel shapes, else 0. */
+int linattn_supported(int map, int dtype, int64_t d_k, int64_t d_v);
+
+/*
+ * phi(x) for every row of x, written to HBM as float32.
+ *   x   [rows, d_k] of `dtype`;  phi [rows, D] float32, D = feature_dim.
+ * Feature maps as defined above ("Simple linear attention ...", Knowl 3).
+ * This export exists for tests and inspection; the attention calls never
+ * materialise phi in HBM (same page, Knowl 5, last paragraph).
+ * Supported: the d_k values listed above.  rows == 0 is a no-op.
+ */
+linattn_status_t linattn_feature_map(int map, int dtype, const void* x,
+                                     int64_t rows, int64_t d_k, float* phi,
+                                     void* stream);
+
+/*
+ * Bytes of device workspace linattn_prefill needs for this shape and
+ * segment length (0 = the library's choice).  May be 0.  Returns (size_t)-1
+ * for invalid or unsupported arguments.
+ */
+size_t linattn_prefill_workspace_bytes(int map, int dtype, int64_t B,
+                                       int64_t H, int64_t N, int64_t d_k,
+                                       int64_t d_v, int64_t seg_len);
+
+/*
+ * Causal prefill: every output y_i of the causal equation above for all
+ * B*H sequences of length N, and optionally the final state for later
+ * generation ("Simple linear attention ...", Knowl 5, first paragraph:
+ * prefill takes q, k, v for B, H, N, d and D, and may write the final
+ * states).
+ *   q  [B, H, N, d_k]   k [B, H, N, d_k]   v [B, H, N, d_v]   (dtype)
+ *   y  [B, H, N, d_v]   (dtype; bf16 results are rounded to nearest even)
+ *   S_in, z_in  [B, H, D, d_v], [B, H, D] float32: the state before token 1,
+ *               or both NULL for the zero state (the sums of the causal
+ *               equation then start at j = 1).
+ *   S_out, z_out [B, H, D, d_v], [B, H, D] float32: the state after token N,
+ *               or both NULL.  S_out may be the same pointer as S_in and
+ *               z_out the same as z_in (in-place continuation); any other
+ *               overlap is an error.
+ *   seg_len     tokens per workgroup segment along N: 0 = library choice,
+ *               else a positive multiple of 64.  Results agree for every
+ *               choice to rounding; each choice is deterministic.
+ *   workspace   device scratch of at least
+ *               linattn_prefill_workspace_bytes(..., seg_len) bytes (may be
+ *               NULL when that is 0).  Its contents on entry do not matter;
+ *               on return they are unspecified.  Two calls in flight at once
+ *               must not share a workspace.
+ * Internally the state is accumulated in float32; bf16 inputs feed bf16
+ * MFMA products with float32 accumulation.
+ */
+linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,
+                                 int64_t N, int64_t d_k, int64_t d_v,
+                                 const void* q, const void* k, const void* v,
+                                 void* y, const float* S_in,
+                                 const float* z_in, float* S_out, float* z_out,
+                                 int64_t seg_len, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * One generation step for all B*H sequences: update the state with the new
+ * token, then read it ("Simple linear attention ...", Knowl 3 recurrent
+ * equations; Knowl 5, second paragraph):
+ *   S += phi(k)^T v;  z += phi(k)^T;  y = phi(q) S / phi(q) z.
+ *   q, k [B, H, d_k]   v [B, H, d_v]   y [B, H, d_v]   (dtype)
+ *   S [B, H, D, d_v], z [B, H, D] float32, read and written in place.
+ * All arithmetic is float32 (inputs are widened); y is rounded to dtype.
+ * y must not overlap S or z.  A zero state is valid input only if the step's
+ * own token makes the denominator positive (it always does: phi(k) > 0 for
+ * ELU1 and phi(q).phi(k) >= 1/2 for TAYLOR2).
+ */
+linattn_status_t linattn_decode_step(int map, int dtype, int64_t B, int64_t H,
+                                     int64_t d_k, int64_t d_v, const void* q,
+                                     const void* k, const void* v, float* S,
+                                     float* z, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,158 @@
+"""The C ABI on the CPU: it builds, loads, exports what the header declares,
+and rejects bad arguments before any HIP call (no GPU is touched here:
+every call below fails validation, which happens before the runtime is
+used)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+from causal_linear_attention_linattn_amd import ops  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        from causal_linear_attention_linattn_amd import _build
+        _build.build()
+    return ops.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(linattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "linattn.h"\nint main(void){return linattn_version() > 0 ? 0 : 1;}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                    "-I", os.path.join(ROOT, "include"), str(src)], check=True)
+
+
+def test_c_program_links(tmp_path, lib):
+    src = tmp_path / "use.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "linattn.h"\n'
+        "int main(void){\n"
+        '  printf("%d %lld\\n", linattn_version(), (long long)linattn_feature_dim(LINATTN_MAP_TAYLOR2, 16));\n'
+        "  return linattn_prefill(0,1,1,1,1,64,64,0,0,0,0,0,0,0,0,0,0,0,0) == LINATTN_ERR_INVALID_ARGUMENT ? 0 : 1;\n"
+        "}\n")
+    exe = tmp_path / "use"
+    libdir = os.path.dirname(ops.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), f"-L{libdir}", "-llinattn",
+                    f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True)
+    assert out.stdout.split() == ["100", "273"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"linattn_prefill", "linattn_decode_step", "linattn_feature_map"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH],
+                        capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (linattn_\w+)", nm))
+    assert set(names) <= exported
+
+
+def test_feature_dim_and_supported(lib):
+    assert lib.linattn_feature_dim(0, 64) == 64
+    assert lib.linattn_feature_dim(1, 16) == 273
+    assert lib.linattn_feature_dim(1, 3) == 13
+    assert lib.linattn_feature_dim(7, 16) == -1
+    assert lib.linattn_feature_dim(0, 0) == -1
+    for dt in (0, 1):
+        for d in (16, 32, 64):
+            assert lib.linattn_supported(0, dt, d, d) == 1
+            assert lib.linattn_supported(1, dt, 16, d) == 1
+        assert lib.linattn_supported(0, dt, 64, 32) == 0
+        assert lib.linattn_supported(0, dt, 128, 128) == 0
+        assert lib.linattn_supported(1, dt, 32, 64) == 0
+    assert lib.linattn_supported(0, 2, 64, 64) == 0
+    for s in range(6):
+        assert lib.linattn_status_string(s)
+
+
+def test_workspace_bytes(lib):
+    f = lib.linattn_prefill_workspace_bytes
+    bad = ctypes.c_size_t(-1).value
+    # one segment per head -> no workspace
+    assert f(0, 1, 1, 2, 256, 16, 16, 0) == 0
+    assert f(0, 1, 64, 64, 4096, 64, 64, 0) == 0
+    # explicit segments: B*H*nseg slots of NRT*NCT*256 floats
+    slot_elu64 = 4 * 5 * 256
+    assert f(0, 1, 8, 8, 4096, 64, 64, 1024) == 64 * 4 * slot_elu64 * 4
+    assert f(0, 1, 8, 8, 4096, 64, 64, 4096) == 0
+    slot_tay = 18 * 5 * 256
+    assert f(1, 1, 8, 16, 2048, 16, 64, 512) == 128 * 4 * slot_tay * 4
+    # ragged: 65 tokens in 64-token segments -> 2 segments
+    assert f(0, 0, 1, 1, 65, 16, 16, 64) == 2 * (2 * 2 * 256) * 4
+    assert f(0, 1, 1, 1, 4096, 64, 64, 100) == bad     # not a multiple of 64
+    assert f(0, 1, 1, 1, 0, 64, 64, 0) == bad
+    assert f(0, 1, 1, 1, 64, 64, 32, 0) == bad         # unsupported
+    assert f(3, 1, 1, 1, 64, 64, 64, 0) == bad
+
+
+# Fake, well separated, 16-byte aligned device addresses: validation only
+# compares and aligns them; it never dereferences anything.
+A = {n: ctypes.c_void_p(0x10000000 * (i + 1)) for i, n in
+     enumerate(["q", "k", "v", "y", "Si", "zi", "So", "zo", "ws"])}
+
+
+def _prefill(lib, **kw):
+    a = dict(map=0, dtype=1, B=1, H=1, N=128, dk=64, dv=64, q=A["q"], k=A["k"],
+             v=A["v"], y=A["y"], Si=None, zi=None, So=None, zo=None, seg=0,
+             ws=None, wsb=0)
+    a.update(kw)
+    return lib.linattn_prefill(a["map"], a["dtype"], a["B"], a["H"], a["N"],
+                               a["dk"], a["dv"], a["q"], a["k"], a["v"], a["y"],
+                               a["Si"], a["zi"], a["So"], a["zo"], a["seg"],
+                               a["ws"], a["wsb"], None)
+
+
+def test_prefill_validation_codes(lib):
+    INV, UNS, WS = 1, 2, 3
+    assert _prefill(lib, q=None) == INV
+    assert _prefill(lib, y=None) == INV
+    assert _prefill(lib, N=0) == INV
+    assert _prefill(lib, B=-1) == INV
+    assert _prefill(lib, map=5) == INV
+    assert _prefill(lib, dtype=9) == INV
+    assert _prefill(lib, dk=48, dv=48) == UNS
+    assert _prefill(lib, q=ctypes.c_void_p(0x10000008)) == INV   # misaligned
+    assert _prefill(lib, Si=A["Si"]) == INV                        # z_in missing
+    assert _prefill(lib, So=A["So"]) == INV                        # z_out missing
+    assert _prefill(lib, y=A["q"]) == INV                          # y aliases q
+    assert _prefill(lib, seg=65) == INV
+    # 2 segments need a workspace
+    assert _prefill(lib, seg=64) == WS
+    assert _prefill(lib, seg=64, ws=A["ws"], wsb=10) == WS
+    assert _prefill(lib, seg=64, ws=ctypes.c_void_p(0x90000004), wsb=1 << 20) == WS
+    # the workspace must not overlap an input
+    assert _prefill(lib, seg=64, ws=A["q"], wsb=1 << 20) == INV
+    # S_out may equal S_in, but must not partially overlap it
+    assert _prefill(lib, Si=A["Si"], zi=A["zi"], So=ctypes.c_void_p(0x50000010),
+                    zo=A["zo"]) == INV
+
+
+def test_decode_and_feature_map_validation(lib):
+    INV, UNS = 1, 2
+    f = lib.linattn_decode_step
+    assert f(1, 1, 4, 16, 16, 64, A["q"], A["k"], A["v"], None, A["zi"], A["y"], None) == INV
+    assert f(1, 1, 4, 16, 16, 64, A["q"], A["k"], A["v"], A["Si"], A["zi"], A["Si"], None) == INV
+    assert f(1, 1, 0, 16, 16, 64, A["q"], A["k"], A["v"], A["Si"], A["zi"], A["y"], None) == INV
+    assert f(1, 1, 4, 16, 32, 64, A["q"], A["k"], A["v"], A["Si"], A["zi"], A["y"], None) == UNS
+    g = lib.linattn_feature_map
+    assert g(0, 1, A["q"], 10, 64, None, None) == INV
+    assert g(1, 1, A["q"], 10, 64, A["y"], None) == UNS
+    assert g(0, 1, A["q"], -1, 64, A["y"], None) == INV
+    assert g(0, 1, A["q"], 0, 64, A["y"], None) == 0   # empty: nothing to do
