@@ -24,9 +24,13 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+# -amdgpu-mfma-vgpr-form: keep MFMA accumulators in ordinary VGPRs (gfx950
+# allows it), which removes the v_accvgpr_read copies before every VALU use
+# of an accumulator.
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
 ]
 

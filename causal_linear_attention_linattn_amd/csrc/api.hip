@@ -22,6 +22,11 @@ constexpr int kVersion = 100;  // 0.1.0
 constexpr int kChunk = 64;     // tokens per chunk inside the prefill kernels
 constexpr int kTargetWorkgroups = 256;  // MI355X compute units
 constexpr int64_t kMinSegChunks = 8;    // shortest default segment (chunks)
+// With at most this many segments per head, each output workgroup adds up
+// its predecessors' segment sums itself; with more, a scan kernel runs.
+constexpr int kDirectPrefixMax = 8;
+// A segment's q/k/v bytes must fit one buffer descriptor (31-bit range).
+constexpr int64_t kMaxSegBytes = ((int64_t)1 << 31) - 4096;
 constexpr int64_t kMaxElems = (int64_t)1 << 46;
 
 #define LINATTN_FOR_SHAPES(X)                                                 \
@@ -84,9 +89,10 @@ Range rng(const void* p, int64_t elems, size_t esz) {
 }
 
 // Segments along N: each workgroup walks seg_chunks consecutive chunks.
-bool plan_segments(int64_t BH, int64_t N, int64_t seg_len, int* nseg_out,
-                   int* seg_chunks_out) {
+bool plan_segments(int64_t BH, int64_t N, int64_t seg_len, int64_t row_bytes,
+                   int* nseg_out, int* seg_chunks_out) {
   const int64_t nchunks = (N + kChunk - 1) / kChunk;
+  const int64_t max_seg_chunks = kMaxSegBytes / (kChunk * row_bytes);
   int64_t seg_chunks;
   if (seg_len == 0) {
     int64_t nseg = (kTargetWorkgroups + BH - 1) / BH;
@@ -100,6 +106,10 @@ bool plan_segments(int64_t BH, int64_t N, int64_t seg_len, int* nseg_out,
     seg_chunks = seg_len / kChunk;
   }
   if (seg_chunks > nchunks) seg_chunks = nchunks;
+  if (seg_chunks > max_seg_chunks) {
+    if (seg_len != 0) return false;
+    seg_chunks = max_seg_chunks;
+  }
   const int64_t nseg = (nchunks + seg_chunks - 1) / seg_chunks;
   if (BH * nseg > INT_MAX || seg_chunks > INT_MAX) return false;
   *nseg_out = (int)nseg;
@@ -203,7 +213,8 @@ size_t linattn_prefill_workspace_bytes(int map, int dtype, int64_t B, int64_t H,
   if (!is_supported(map, dtype, d_k, d_v)) return (size_t)-1;
   if (B > kMaxElems / H || N > kMaxElems / (B * H)) return (size_t)-1;
   int nseg, seg_chunks;
-  if (!plan_segments(B * H, N, seg_len, &nseg, &seg_chunks)) return (size_t)-1;
+  const int64_t row_bytes = (d_k > d_v ? d_k : d_v) * (int64_t)elem_size(dtype);
+  if (!plan_segments(B * H, N, seg_len, row_bytes, &nseg, &seg_chunks)) return (size_t)-1;
   return workspace_bytes(map, B * H, d_k, d_v, nseg);
 }
 
@@ -232,7 +243,8 @@ linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,
       (S_out && (!aligned4(S_out) || !aligned4(z_out))))
     return LINATTN_ERR_INVALID_ARGUMENT;
   int nseg, seg_chunks;
-  if (!plan_segments(BH, N, seg_len, &nseg, &seg_chunks))
+  const int64_t row_bytes = (d_k > d_v ? d_k : d_v) * (int64_t)elem_size(dtype);
+  if (!plan_segments(BH, N, seg_len, row_bytes, &nseg, &seg_chunks))
     return LINATTN_ERR_INVALID_ARGUMENT;
 
   const size_t es = elem_size(dtype);
@@ -280,6 +292,7 @@ linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,
   a.BH = (int)BH;
   a.nseg = nseg;
   a.seg_chunks = seg_chunks;
+  a.prefix_mode = nseg == 1 ? 0 : (nseg <= kDirectPrefixMax ? 1 : 2);
   const hipError_t e =
       dispatch_prefill(map, dtype, d_k, d_v, a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;

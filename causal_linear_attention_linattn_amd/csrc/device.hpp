@@ -33,8 +33,23 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(bf16_t, h);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane 4i + j passes the
+// address of 4 consecutive 16-bit elements (row i, columns 4j..4j+3 of a
+// 4 x 16 block); lane c receives column c of the 4 rows.
+__device__ __forceinline__ uint2 lds_read_tr4(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+  const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
 }
 
 // Workgroup barrier that orders LDS traffic only.  __syncthreads() would
@@ -44,6 +59,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Raw buffer resource over [base, base + bytes): loads outside the range
+// return zero (hardware range check), so tails need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                           uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                          (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r,
+                                               uint32_t byte_offset) {
+  return __builtin_bit_cast(
+      uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
 }
 
 __device__ __forceinline__ float phi_elu1(float x) {
@@ -71,16 +100,12 @@ template <> struct Elem<bf16_t> {
     return f32_to_bf16(x);
   }
   __device__ static __forceinline__ frag make(const float (&v)[8]) {
-    frag f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (__bf16)v[i];
-    return f;
+    const uint4 u = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    return __builtin_bit_cast(frag, u);
   }
   __device__ static __forceinline__ frag zero() {
-    frag f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (__bf16)0.0f;
-    return f;
+    return __builtin_bit_cast(frag, make_uint4(0u, 0u, 0u, 0u));
   }
   // 8 consecutive elements, 16-byte aligned (LDS or global).
   __device__ static __forceinline__ frag load8(const bf16_t* p) {
@@ -179,6 +204,16 @@ template <>
 __device__ __forceinline__ uint4 pack16<float>(const float (&v)[4]) {
   return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
                     __float_as_uint(v[2]), __float_as_uint(v[3]));
+}
+
+// Two consecutive elements (a token pair of one transposed row) in one
+// LDS store: 4 bytes for bf16, 8 bytes for float.
+__device__ __forceinline__ void store_pair(bf16_t* p, float a, float b) {
+  *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
+}
+
+__device__ __forceinline__ void store_pair(float* p, float a, float b) {
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
 }
 
 }  // namespace linattn

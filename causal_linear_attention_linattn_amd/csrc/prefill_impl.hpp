@@ -53,15 +53,25 @@ struct PrefillShape : StateShape<MAP, DK, DV> {
   static constexpr int KS = DK + EPU;       // LDS row strides (elements),
   static constexpr int CS = C + EPU;        // padded by 16 bytes
   static constexpr int PS = SS::DP + EPU;
+  static constexpr int KUR = DK / EPU;      // 16-byte units per k row
+  static constexpr int VUR = DV / EPU;
   static constexpr int UK = C * DK / EPU;   // 16-byte units per k tile
   static constexpr int UV = C * DV / EPU;
   static constexpr int NUK = (UK + NT - 1) / NT;
   static constexpr int NUV = (UV + NT - 1) / NT;
-  static constexpr int KUR = DK / EPU;      // units per k row
-  static constexpr int VUR = DV / EPU;
+  static constexpr int PK = C / 2 * KUR;    // row-pair units per k tile
+  static constexpr int PV = C / 2 * VUR;
+  static constexpr int NPK = (PK + NT - 1) / NT;
+  static constexpr int NPV = (PV + NT - 1) / NT;
   static constexpr int NQU = MAP == MAP_ELU1 ? SS::NKB * 8 / EPU : DK / EPU;
   static constexpr int NKBS = (DK + 31) / 32;  // K blocks of the scores
 };
+
+// Chunks in the register prefetch ring of the chunk walker (P - 1 chunks in
+// flight while one is computed): the light segment-sum pass affords three
+// stages, the output pass two.
+template <bool OUT>
+constexpr int kRing = OUT ? 2 : 3;
 
 // Internal feature row -> exported row (or -1 for padding) and the factor
 // that converts an exported value into the internal one.
@@ -123,22 +133,71 @@ __device__ __forceinline__ void state_out_tile(float* S_out, float* z_out,
   }
 }
 
+// Row-major bf16 tile of R-element rows in LDS.  16-byte units within a
+// row are XOR-swizzled by the row index, and rows are padded to R + 32
+// elements, so that the row stores of the staging pass, the 16-byte row
+// reads and the transposed 8-byte reads below stay (nearly) free of bank
+// conflicts.
+template <int R>
+struct RowTile {
+  static constexpr int UPR = R / 8;  // 16-byte units per row
+  static constexpr int STRIDE = R + 32;
+  __device__ static __forceinline__ int off(int row, int unit) {
+    return row * STRIDE + 8 * (unit ^ ((row ^ (row >> 3)) & (UPR - 1)));
+  }
+  __device__ static __forceinline__ int off_el(int row, int col) {
+    return off(row, col >> 3) + (col & 7);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // The chunk walker.  OUT = false: sum phi(K)^T V' over the segment and store
 // it in workspace slot seg + 1 (segments 0 .. nseg-2).  OUT = true: produce
 // y for the segment starting from its prefix state.
+//
+// Global loads are raw buffer loads whose range is the segment itself, so
+// rows past the segment end (or past N) read as zero without a branch.  The
+// next P - 1 chunks are in flight in registers while one chunk is computed.
+//
+// Operands contracted over tokens (phi(K)^T and V' in the state update, V'^T
+// in the within-chunk product) need 8 consecutive tokens per lane.  bf16
+// tiles are kept row-major and read with the LDS transpose read; float
+// tiles are stored transposed (two tokens per store).
 // ---------------------------------------------------------------------------
+template <class SH, bool BF>
+struct Stage {
+  static constexpr int NK = BF ? SH::NUK : 2 * SH::NPK;
+  static constexpr int NV = BF ? SH::NUV : 2 * SH::NPV;
+  uint4 k[NK];
+  uint4 v[NV];
+  uint4 q[SH::NQU];
+};
+
 template <int MAP, typename T, int DK, int DV, bool OUT>
 __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   using SH = PrefillShape<MAP, T, DK, DV>;
   using E = Elem<T>;
   using frag = typename E::frag;
+  constexpr bool BF = sizeof(T) == 2;
   constexpr int C = SH::C, NCT = SH::NCT, NRT = SH::NRT, NKB = SH::NKB;
   constexpr int KS = SH::KS, CS = SH::CS, PS = SH::PS, EPU = SH::EPU;
+  constexpr int P = kRing<OUT>;
+  constexpr uint32_t ES = sizeof(T);
+  constexpr uint32_t kOOB = 0x7ffffff0u;  // an offset no segment reaches
+  using RTK = RowTile<DK>;
+  using RTV = RowTile<DV>;
+  using St = Stage<SH, BF>;
 
-  __shared__ __align__(16) T sK[OUT ? C * KS : EPU];
-  __shared__ __align__(16) T sKT[DK * CS];
-  __shared__ __align__(16) T sVT[DV * CS];
+  // sK: rows of phi(K) (ELU1) or k (TAYLOR2); needed by the output kernel
+  // for the scores and, for bf16 ELU1, by both kernels as the transposed
+  // source of phi(K)^T.  sKT: K transposed (float, and TAYLOR2).
+  constexpr bool kNeedK = OUT || (BF && MAP == MAP_ELU1);
+  constexpr bool kNeedKT = !(BF && MAP == MAP_ELU1);
+  constexpr int K_EL = BF ? C * RTK::STRIDE : C * KS;
+  constexpr int V_EL = BF ? C * RTV::STRIDE : DV * CS;
+  __shared__ __align__(16) T sK[kNeedK ? K_EL : EPU];
+  __shared__ __align__(16) T sKT[kNeedKT ? DK * CS : EPU];
+  __shared__ __align__(16) T sV[V_EL];
   __shared__ __align__(16) T sS[OUT ? SH::NCOL * PS : EPU];
 
   const int tid = threadIdx.x;
@@ -154,11 +213,15 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   const int64_t tok_begin = (int64_t)seg * a.seg_chunks * C;
   int64_t tok_end = tok_begin + (int64_t)a.seg_chunks * C;
   if (tok_end > N) tok_end = N;
-  const int nchunks = (int)((tok_end - tok_begin + C - 1) / C);
+  const int ntok = (int)(tok_end - tok_begin);   // tokens in this segment
+  const int nchunks = (ntok + C - 1) / C;
 
-  const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)bh * N * DK;
-  const T* kg = reinterpret_cast<const T*>(a.k) + (size_t)bh * N * DK;
-  const T* vg = reinterpret_cast<const T*>(a.v) + (size_t)bh * N * DV;
+  const T* qg = reinterpret_cast<const T*>(a.q) + ((size_t)bh * N + tok_begin) * DK;
+  const T* kg = reinterpret_cast<const T*>(a.k) + ((size_t)bh * N + tok_begin) * DK;
+  const T* vg = reinterpret_cast<const T*>(a.v) + ((size_t)bh * N + tok_begin) * DV;
+  const auto rq = make_rsrc(qg, (uint32_t)ntok * DK * ES);
+  const auto rk = make_rsrc(kg, (uint32_t)ntok * DK * ES);
+  const auto rv = make_rsrc(vg, (uint32_t)ntok * DV * ES);
 
   // ------------------------------------------------------------ state ----
   f32x4_t Sacc[SH::MAXRT][NCT];
@@ -169,12 +232,20 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
       if (OUT && rt < NRT) {
-        if (a.nseg > 1) {
+        if (a.prefix_mode == 2) {
+          // scanned workspace: slot seg holds the exclusive prefix
           const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
               a.ws + ((size_t)bh * a.nseg + seg) * SH::SLOT);
           s = p[(rt * NCT + ct) * 64 + lane];
-        } else if (a.S_in != nullptr) {
-          s = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, bh, rt, ct, lane);
+        } else {
+          if (a.S_in != nullptr)
+            s = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, bh, rt, ct, lane);
+          // few segments: add the sums of the preceding segments directly
+          for (int j = 1; j <= seg; ++j) {
+            const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
+                a.ws + ((size_t)bh * a.nseg + j) * SH::SLOT);
+            s += p[(rt * NCT + ct) * 64 + lane];
+          }
         }
       }
       Sacc[m][ct] = s;
@@ -187,87 +258,166 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   for (int t = 0; t < 8; ++t) onesv[t] = i16 == 0 ? 1.0f : 0.0f;
   const frag ones = E::make(onesv);
 
-  // ---------------------------------------------------------- staging ----
-  uint4 kreg[SH::NUK], vreg[SH::NUV], qreg[OUT ? SH::NQU : 1];
-  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-
-  auto issue_loads = [&](int c) {
-    const int64_t t0 = tok_begin + (int64_t)c * C;
-    const bool chunk_ok = c < nchunks;
-#pragma unroll
-    for (int u = 0; u < SH::NUK; ++u) {
-      const int unit = tid + u * SH::NT;
-      const int r = unit / SH::KUR;
-      const int e0 = (unit % SH::KUR) * EPU;
-      kreg[u] = z4;
-      if (unit < SH::UK && chunk_ok && t0 + r < tok_end)
-        kreg[u] = *reinterpret_cast<const uint4*>(kg + (t0 + r) * DK + e0);
+  // ------------------------------------------------- tile operand access --
+  // 8 tokens (tb .. tb+7) of column c0 + i16 of a row-major bf16 tile
+  auto tokfrag_bf = [&](const T* base, int stride_el, int upr_mask, int tb, int c0) -> frag {
+    if constexpr (BF) {
+      const int r = tb + (i16 >> 2);
+      const int col = c0 + 4 * (i16 & 3);
+      auto off = [&](int row) {
+        return row * stride_el + 8 * ((col >> 3) ^ ((row ^ (row >> 3)) & upr_mask)) + (col & 7);
+      };
+      const uint2 lo = lds_read_tr4(reinterpret_cast<const uint16_t*>(base) + off(r));
+      const uint2 hi = lds_read_tr4(reinterpret_cast<const uint16_t*>(base) + off(r + 4));
+      return __builtin_bit_cast(frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    } else {
+      return E::zero();
     }
+  };
+
+  // V' / V'^T operand: lane (column i16 of tile ct, g) slot t <-> token
+  // 32 jb2 + 8 g + t
+  auto v_frag = [&](int jb2, int ct) -> frag {
+    if constexpr (BF)
+      return tokfrag_bf(sV, RTV::STRIDE, RTV::UPR - 1, 32 * jb2 + 8 * g, 16 * ct);
+    else
+      return E::load8(sV + (16 * ct + i16) * CS + 32 * jb2 + 8 * g);
+  };
+
+  // ---------------------------------------------------------- staging ----
+  St st[P];
+
+  auto issue = [&](int c, St& s) {
+    const uint32_t cb = (uint32_t)c * C;  // first token of chunk c
+    if constexpr (BF) {
 #pragma unroll
-    for (int u = 0; u < SH::NUV; ++u) {
-      const int unit = tid + u * SH::NT;
-      const int r = unit / SH::VUR;
-      const int e0 = (unit % SH::VUR) * EPU;
-      vreg[u] = z4;
-      if (unit < SH::UV && chunk_ok && t0 + r < tok_end)
-        vreg[u] = *reinterpret_cast<const uint4*>(vg + (t0 + r) * DV + e0);
+      for (int u = 0; u < St::NK; ++u) {
+        const int p = tid + u * SH::NT;
+        const uint32_t off = ((cb + p / RTK::UPR) * DK + (p % RTK::UPR) * 8) * ES;
+        s.k[u] = buffer_load16(rk, p < SH::UK ? off : kOOB);
+      }
+#pragma unroll
+      for (int u = 0; u < St::NV; ++u) {
+        const int p = tid + u * SH::NT;
+        const uint32_t off = ((cb + p / RTV::UPR) * DV + (p % RTV::UPR) * 8) * ES;
+        s.v[u] = buffer_load16(rv, p < SH::UV ? off : kOOB);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < SH::NPK; ++u) {
+        const int pu = tid + u * SH::NT;
+        const uint32_t r0 = cb + 2 * (pu / SH::KUR);
+        const uint32_t e0 = (pu % SH::KUR) * EPU;
+        const uint32_t off = pu < SH::PK ? (r0 * DK + e0) * ES : kOOB;
+        s.k[2 * u] = buffer_load16(rk, off);
+        s.k[2 * u + 1] = buffer_load16(rk, pu < SH::PK ? off + DK * ES : kOOB);
+      }
+#pragma unroll
+      for (int u = 0; u < SH::NPV; ++u) {
+        const int pu = tid + u * SH::NT;
+        const uint32_t r0 = cb + 2 * (pu / SH::VUR);
+        const uint32_t e0 = (pu % SH::VUR) * EPU;
+        const uint32_t off = pu < SH::PV ? (r0 * DV + e0) * ES : kOOB;
+        s.v[2 * u] = buffer_load16(rv, off);
+        s.v[2 * u + 1] = buffer_load16(rv, pu < SH::PV ? off + DV * ES : kOOB);
+      }
     }
     if constexpr (OUT) {
-      const int64_t tq = t0 + 16 * w + i16;
-      const bool ok = chunk_ok && tq < tok_end;
+      const uint32_t tq = cb + 16 * w + i16;
       if constexpr (MAP == MAP_ELU1) {
         constexpr int UPB = 8 / EPU;  // 16-byte units per 8-feature block
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int h = 0; h < UPB; ++h) {
-            const int f0 = 32 * kb + 8 * g + h * EPU;
-            qreg[kb * UPB + h] = z4;
-            if (ok && f0 < DK)
-              qreg[kb * UPB + h] =
-                  *reinterpret_cast<const uint4*>(qg + tq * DK + f0);
+            const uint32_t f0 = 32 * kb + 8 * g + h * EPU;
+            s.q[kb * UPB + h] = buffer_load16(rq, f0 < DK ? (tq * DK + f0) * ES : kOOB);
           }
       } else {
 #pragma unroll
-        for (int u = 0; u < SH::NQU; ++u) {
-          qreg[u] = z4;
-          if (ok)
-            qreg[u] = *reinterpret_cast<const uint4*>(qg + tq * DK + u * EPU);
-        }
+        for (int u = 0; u < SH::NQU; ++u)
+          s.q[u] = buffer_load16(rq, (tq * DK + u * EPU) * ES);
       }
     }
   };
 
-  auto write_tiles = [&](int c) {
-    const int64_t t0 = tok_begin + (int64_t)c * C;
+  // Stage chunk c into LDS.
+  auto write_tiles = [&](int c, const St& s) {
+    const int cb = c * C;
+    const bool full = cb + C <= ntok;  // no row past the segment end
+    if constexpr (BF) {
 #pragma unroll
-    for (int u = 0; u < SH::NUK; ++u) {
-      const int unit = tid + u * SH::NT;
-      if (unit < SH::UK) {
-        const int r = unit / SH::KUR;
-        const int e0 = (unit % SH::KUR) * EPU;
-        const bool ok = t0 + r < tok_end;
-        float f[EPU];
-        unpack16<T>(kreg[u], f);
-        if constexpr (MAP == MAP_ELU1) {
+      for (int u = 0; u < St::NK; ++u) {
+        const int p = tid + u * SH::NT;
+        if (SH::UK % SH::NT == 0 || p < SH::UK) {  // compile-time when tiles divide evenly
+          const int row = p / RTK::UPR, unit = p % RTK::UPR;
+          if constexpr (MAP == MAP_ELU1) {
+            float f[8];
+            unpack16<T>(s.k[u], f);
+            if (full) {
 #pragma unroll
-          for (int e = 0; e < EPU; ++e) f[e] = ok ? phi_elu1(f[e]) : 0.0f;
+              for (int e = 0; e < 8; ++e) f[e] = phi_elu1(f[e]);
+            } else {
+              const bool ok = cb + row < ntok;  // phi(0) = 1: zero the pad
+#pragma unroll
+              for (int e = 0; e < 8; ++e) f[e] = ok ? phi_elu1(f[e]) : 0.0f;
+            }
+            *reinterpret_cast<uint4*>(sK + RTK::off(row, unit)) = pack16<T>(f);
+          } else {
+            if constexpr (OUT) *reinterpret_cast<uint4*>(sK + RTK::off(row, unit)) = s.k[u];
+            const uint32_t wd[4] = {s.k[u].x, s.k[u].y, s.k[u].z, s.k[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sKT[(unit * 8 + 2 * e) * CS + row] = (bf16_t)(wd[e] & 0xffffu);
+              sKT[(unit * 8 + 2 * e + 1) * CS + row] = (bf16_t)(wd[e] >> 16);
+            }
+          }
         }
-        if constexpr (OUT) *reinterpret_cast<uint4*>(sK + r * KS + e0) = pack16<T>(f);
-#pragma unroll
-        for (int e = 0; e < EPU; ++e) sKT[(e0 + e) * CS + r] = E::from_f32(f[e]);
       }
-    }
 #pragma unroll
-    for (int u = 0; u < SH::NUV; ++u) {
-      const int unit = tid + u * SH::NT;
-      if (unit < SH::UV) {
-        const int r = unit / SH::VUR;
-        const int e0 = (unit % SH::VUR) * EPU;
-        float f[EPU];
-        unpack16<T>(vreg[u], f);
+      for (int u = 0; u < St::NV; ++u) {
+        const int p = tid + u * SH::NT;
+        if (SH::UV % SH::NT == 0 || p < SH::UV)
+          *reinterpret_cast<uint4*>(sV + RTV::off(p / RTV::UPR, p % RTV::UPR)) = s.v[u];
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < EPU; ++e) sVT[(e0 + e) * CS + r] = E::from_f32(f[e]);
+      for (int u = 0; u < SH::NPK; ++u) {
+        const int pu = tid + u * SH::NT;
+        if (SH::PK % SH::NT == 0 || pu < SH::PK) {
+          const int r0 = 2 * (pu / SH::KUR);
+          const int e0 = (pu % SH::KUR) * EPU;
+          float f0[EPU], f1[EPU];
+          unpack16<T>(s.k[2 * u], f0);
+          unpack16<T>(s.k[2 * u + 1], f1);
+          if constexpr (MAP == MAP_ELU1) {
+            const bool ok0 = cb + r0 < ntok, ok1 = cb + r0 + 1 < ntok;
+#pragma unroll
+            for (int e = 0; e < EPU; ++e) {
+              f0[e] = ok0 ? phi_elu1(f0[e]) : 0.0f;
+              f1[e] = ok1 ? phi_elu1(f1[e]) : 0.0f;
+            }
+          }
+          if constexpr (OUT) {
+            *reinterpret_cast<uint4*>(sK + r0 * KS + e0) = pack16<T>(f0);
+            *reinterpret_cast<uint4*>(sK + (r0 + 1) * KS + e0) = pack16<T>(f1);
+          }
+#pragma unroll
+          for (int e = 0; e < EPU; ++e) store_pair(sKT + (e0 + e) * CS + r0, f0[e], f1[e]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < SH::NPV; ++u) {
+        const int pu = tid + u * SH::NT;
+        if (SH::PV % SH::NT == 0 || pu < SH::PV) {
+          const int r0 = 2 * (pu / SH::VUR);
+          const int e0 = (pu % SH::VUR) * EPU;
+          float f0[EPU], f1[EPU];
+          unpack16<T>(s.v[2 * u], f0);
+          unpack16<T>(s.v[2 * u + 1], f1);
+#pragma unroll
+          for (int e = 0; e < EPU; ++e) store_pair(sV + (e0 + e) * CS + r0, f0[e], f1[e]);
+        }
       }
     }
   };
@@ -279,7 +429,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   float qv[MAP == MAP_TAYLOR2 && OUT ? DK : 1];
   float qb8[MAP == MAP_TAYLOR2 && OUT ? 8 : 1];
 
-  auto take_q = [&]() {
+  auto take_q = [&](const St& s) {
     if constexpr (!OUT) return;
     if constexpr (MAP == MAP_ELU1) {
       constexpr int UPB = 8 / EPU;
@@ -289,7 +439,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
         for (int h = 0; h < UPB; ++h) {
           float part[EPU];
-          unpack16<T>(qreg[kb * UPB + h], part);
+          unpack16<T>(s.q[kb * UPB + h], part);
 #pragma unroll
           for (int e = 0; e < EPU; ++e) f[h * EPU + e] = part[e];
         }
@@ -302,7 +452,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
       for (int u = 0; u < SH::NQU; ++u) {
         float part[EPU];
-        unpack16<T>(qreg[u], part);
+        unpack16<T>(s.q[u], part);
 #pragma unroll
         for (int e = 0; e < EPU; ++e) qv[u * EPU + e] = part[e];
       }
@@ -317,7 +467,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     const int col = 32 * jb2 + 8 * g;
     if constexpr (MAP == MAP_ELU1) {
       if (16 * rt >= DK) return E::zero();
-      return E::load8(sKT + (16 * rt + i16) * CS + col);
+      if constexpr (BF)
+        return tokfrag_bf(sK, RTK::STRIDE, RTK::UPR - 1, col, 16 * rt);
+      else
+        return E::load8(sKT + (16 * rt + i16) * CS + col);
     } else {
       float f[8];
       if (rt < 16) {
@@ -340,6 +493,16 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       }
       return E::make(f);
     }
+  };
+
+  // key rows for the scores: lane (key jt, g) slot t <-> feature 32 kbs + 8 g + t
+  auto k_rows = [&](int jt, int kbs) -> frag {
+    const int f0 = 32 * kbs + 8 * g;
+    if (f0 >= DK) return E::zero();
+    if constexpr (BF)
+      return E::load8(sK + RTK::off(jt, f0 >> 3));
+    else
+      return E::load8(sK + jt * KS + f0);
   };
 
   // phi(Q) operand for feature block kb: lane (query i16, g) slot t <->
@@ -376,7 +539,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       for (int ct = 0; ct < NCT; ++ct) {
         T* p = sS + (16 * ct + i16) * PS + 16 * rt + 4 * g;
         const f32x4_t s = Sacc[m][ct];
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (BF) {
           *reinterpret_cast<uint2*>(p) =
               make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
         } else {
@@ -386,30 +549,18 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     }
   };
 
-  // ------------------------------------------------------------ prologue --
-  issue_loads(0);
-  if constexpr (OUT) publish_state();
-  write_tiles(0);
-  take_q();
-  issue_loads(1);
-  lds_barrier();
+  T* yg = OUT ? reinterpret_cast<T*>(a.y) + ((size_t)bh * N + tok_begin) * DV : nullptr;
 
-  T* yg = OUT ? reinterpret_cast<T*>(a.y) + (size_t)bh * N * DV : nullptr;
+  // One chunk: outputs (OUT) and the state update, then stage chunk c + 1
+  // from the ring slot `nx` and refill that slot with chunk c + P.
+  auto iteration = [&](int c, St& nx) {
+    const int cb = c * C;
+    const int nvalid = ntok - cb < C ? ntok - cb : C;
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int64_t t0 = tok_begin + (int64_t)c * C;
-    const int nvalid = (int)((tok_end - t0) < C ? (tok_end - t0) : C);
-
-    // V'^T / V' operands for the two 32-token key blocks.
-    frag vf[2][NCT - 1];
-#pragma unroll
-    for (int jb2 = 0; jb2 < 2; ++jb2)
-#pragma unroll
-      for (int ct = 0; ct < NCT - 1; ++ct)
-        vf[jb2][ct] = E::load8(sVT + (16 * ct + i16) * CS + 32 * jb2 + 8 * g);
-
+    f32x4_t O[OUT ? NCT : 1];
+    frag qraw = E::zero();
+    const int il = 16 * w + i16;
     if constexpr (OUT) {
-      f32x4_t O[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) O[ct] = {0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -423,19 +574,24 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
           E::mma(O[ct], av, bq);
         }
       }
-
-      // within-chunk term: scores^T for keys <= this wave's queries
-      frag qraw = E::zero();
       if constexpr (MAP == MAP_TAYLOR2) {
         float f[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) f[t] = g < 2 ? qb8[t] : 0.0f;
         qraw = E::make(f);
       }
-      const int il = 16 * w + i16;
+    }
+
+    // Per 32-token key block: the V' operands serve both the within-chunk
+    // product (A-operand, V'^T) and the state update (B-operand, V').
 #pragma unroll
-      for (int jb2 = 0; jb2 < 2; ++jb2) {
-        if (32 * jb2 > 16 * w + 15) continue;
+    for (int jb2 = 0; jb2 < 2; ++jb2) {
+      frag vf[NCT - 1];
+#pragma unroll
+      for (int ct = 0; ct < NCT - 1; ++ct) vf[ct] = v_frag(jb2, ct);
+
+      if (OUT && 32 * jb2 <= 16 * w + 15) {
+        // within-chunk term: scores^T for keys <= this wave's queries
         f32x4_t sc[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -443,42 +599,62 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
           const int jt = 32 * jb2 + 8 * (i16 >> 2) + 4 * h + (i16 & 3);
 #pragma unroll
           for (int kbs = 0; kbs < SH::NKBS; ++kbs) {
-            const int f0 = 32 * kbs + 8 * g;
-            const frag ak = E::load8(sK + jt * KS + (f0 < DK ? f0 : 0));
-            const frag akz = f0 < DK ? ak : E::zero();
             frag bq;
             if constexpr (MAP == MAP_ELU1) bq = q_frag(kbs); else bq = qraw;
-            E::mma(sc[h], akz, bq);
+            E::mma(sc[h], k_rows(jt, kbs), bq);
           }
         }
+        // keys of this block are all <= every query of the wave unless the
+        // block reaches past the wave's first query
+        const bool diag = 32 * jb2 + 31 > 16 * w;
         float f[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const int jl = 32 * jb2 + 8 * g + 4 * h + t;
-            const float s = sc[h][t];
+            const float sv = sc[h][t];
             float val;
-            if constexpr (MAP == MAP_ELU1) val = s; else val = 1.0f + s + 0.5f * s * s;
-            f[4 * h + t] = jl <= il ? val : 0.0f;
+            if constexpr (MAP == MAP_ELU1) val = sv; else val = 1.0f + sv + 0.5f * sv * sv;
+            f[4 * h + t] = val;
           }
-        const frag bA = E::make(f);
+        if (diag) {
 #pragma unroll
-        for (int ct = 0; ct < NCT - 1; ++ct) E::mma(O[ct], vf[jb2][ct], bA);
-        E::mma(O[NCT - 1], ones, bA);
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (32 * jb2 + 8 * g + 4 * h + t > il) f[4 * h + t] = 0.0f;
+        }
+        const frag bA = E::make(f);
+        if constexpr (OUT) {
+#pragma unroll
+          for (int ct = 0; ct < NCT - 1; ++ct) E::mma(O[ct], vf[ct], bA);
+          E::mma(O[NCT - 1], ones, bA);
+        }
       }
 
+      // state update: S' += phi(K)^T V' for this wave's row tiles
+#pragma unroll
+      for (int m = 0; m < SH::MAXRT; ++m) {
+        const int rt = w + 4 * m;
+        if (rt >= NRT) continue;
+        const frag ak = kt_frag(rt, jb2, nvalid);
+#pragma unroll
+        for (int ct = 0; ct < NCT - 1; ++ct) E::mma(Sacc[m][ct], ak, vf[ct]);
+        E::mma(Sacc[m][NCT - 1], ak, ones);
+      }
+    }
+
+    if constexpr (OUT) {
       // normalise and write y (query il of this chunk)
       const float den = __shfl(O[NCT - 1][0], i16, 64);
       const float rden = 1.0f / den;
-      const int64_t tq = t0 + il;
-      if (tq < tok_end) {
-        T* yrow = yg + tq * DV;
+      if (cb + il < ntok) {
+        T* yrow = yg + (size_t)(cb + il) * DV;
 #pragma unroll
         for (int ct = 0; ct < NCT - 1; ++ct) {
           const f32x4_t o = O[ct];
           T* p = yrow + 16 * ct + 4 * g;
-          if constexpr (sizeof(T) == 2) {
+          if constexpr (BF) {
             *reinterpret_cast<uint2*>(p) =
                 make_uint2(pack_bf16x2(o[0] * rden, o[1] * rden),
                            pack_bf16x2(o[2] * rden, o[3] * rden));
@@ -490,28 +666,40 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       }
     }
 
-    // state update: S' += phi(K)^T V' for this wave's row tiles
-#pragma unroll
-    for (int m = 0; m < SH::MAXRT; ++m) {
-      const int rt = w + 4 * m;
-      if (rt >= NRT) continue;
-#pragma unroll
-      for (int jb2 = 0; jb2 < 2; ++jb2) {
-        const frag ak = kt_frag(rt, jb2, nvalid);
-#pragma unroll
-        for (int ct = 0; ct < NCT - 1; ++ct) E::mma(Sacc[m][ct], ak, vf[jb2][ct]);
-        E::mma(Sacc[m][NCT - 1], ak, ones);
-      }
-    }
-
     lds_barrier();  // every wave is done reading the tiles and sS
     if constexpr (OUT) publish_state();
-    if (c + 1 < nchunks) {
-      write_tiles(c + 1);
-      take_q();
-      issue_loads(c + 2);
-    }
+    // Stage chunk c + 1 even past the end: its loads are out of range and
+    // read zeros, and nothing reads those tiles.  An unconditional staging
+    // step keeps the compiler's count of loads in flight exact.
+    write_tiles(c + 1, nx);
+    take_q(nx);
+    issue(c + 1 + P, nx);
+    // keep the loads here: without this fence the compiler sinks them to
+    // their use P - 1 chunks later, which leaves nothing in flight
+    asm volatile("" ::: "memory");
     lds_barrier();
+  };
+
+  // ------------------------------------------------------------ prologue --
+#pragma unroll
+  for (int s = 0; s < P; ++s) issue(s, st[s]);
+  asm volatile("" ::: "memory");
+  if constexpr (OUT) publish_state();
+  write_tiles(0, st[0]);
+  take_q(st[0]);
+  issue(P, st[0]);
+  asm volatile("" ::: "memory");
+  lds_barrier();
+
+  // Chunk c is staged from ring slot c % P; unrolling by P keeps every ring
+  // index a compile-time constant.  The loop runs whole trips of P chunks
+  // with no branch between the copies; chunks past the segment end are
+  // inert (their loads are out of range and read zeros, phi(K) and the
+  // constant Taylor feature are masked to zero there, and no y row is
+  // written), so at most P - 1 empty chunks are walked at the end.
+  for (int c0 = 0; c0 < nchunks; c0 += P) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) iteration(c0 + s, st[(s + 1) % P]);
   }
 
   // ------------------------------------------------------------ epilogue --
@@ -542,6 +730,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 
 // Exclusive prefix over segments, in place: slot s <- init + sum_{p<s} T_p,
 // where slot p+1 held segment p's sum T_p and init is the initial state.
+// Used when there are too many segments per head for each output workgroup
+// to add up its predecessors' sums itself.
 template <int MAP, int DK, int DV>
 __global__ __launch_bounds__(256) void seg_scan_kernel(PrefillArgs a) {
   using SS = StateShape<MAP, DK, DV>;
@@ -570,10 +760,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.nseg > 1) {
     hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, false>),
                        dim3(a.BH * (a.nseg - 1)), dim3(256), 0, st, a);
-    const int64_t threads = (int64_t)a.BH * (SS::SLOT / 4);
-    hipLaunchKernelGGL((seg_scan_kernel<MAP, DK, DV>),
-                       dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       st, a);
+    if (a.prefix_mode == 2) {
+      const int64_t threads = (int64_t)a.BH * (SS::SLOT / 4);
+      hipLaunchKernelGGL((seg_scan_kernel<MAP, DK, DV>),
+                         dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                         st, a);
+    }
   }
   hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, true>),
                      dim3(a.BH * a.nseg), dim3(256), 0, st, a);

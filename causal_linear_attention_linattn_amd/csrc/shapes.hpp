@@ -23,6 +23,8 @@ struct PrefillArgs {
   int BH;
   int nseg;        // segments per (batch, head)
   int seg_chunks;  // chunks per segment
+  int prefix_mode; // 0: one segment; 1: output workgroups add the preceding
+                   // segment sums themselves; 2: a scan kernel runs first
 };
 
 template <int MAP, int DK, int DV>
