@@ -141,6 +141,46 @@ def time_decode(args, ops, synth, torch):
     return cfg, ms_step, ok
 
 
+def csrc_digest():
+    """Hash of the HIP sources; a traffic figure is valid only for this hash."""
+    import hashlib
+
+    d = hashlib.sha256()
+    csrc = os.path.join(ROOT, "causal_linear_attention_linattn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            d.update(name.encode() + b"\0" + f.read())
+    return d.hexdigest()[:16]
+
+
+def recorded_traffic(kind):
+    """HBM bytes per call recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    passes (profiles/traffic.txt), scaled by the plain-copy calibration.
+    None when the file is missing or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest = csrc_digest()
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 3 and parts[0] == kind and parts[1] == digest:
+            return float(parts[2])
+    return None
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size (256 MiB read + 256 MiB written),
+    run under rocprofv3 --pmc to scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 3}))
+
+
 def cpu_baseline(synth, budget_s=20.0):
     """The float64 oracle (recurrent form) on whole batch elements of the
     prefill workload, one element at a time until the time budget is used."""
@@ -207,6 +247,8 @@ def main():
                     help="128-step generations timed for the decode figure")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the plain copy used to scale HBM counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -228,6 +270,9 @@ def main():
         __graft_entry__.build()
     ops.load_library()
     torch.cuda.init()
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     cfg, ms, nsets = time_prefill(args, ops, synth, torch)
     tokens = cfg["B"] * cfg["N"]
@@ -256,8 +301,10 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "linattn_prefill (segment sums + scan + chunk outputs)",
+            "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic("prefill"),
+            "kernel": ("linattn_prefill call: segment-sum pass + chunk-output "
+                       "pass (one kernel when a head is one segment)"),
+            "csrc_digest": csrc_digest(),
             "algorithmic_bytes": nbytes,
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         },
@@ -275,7 +322,8 @@ def main():
                          f"{dcfg['steps']} steps x {args.decode_reps}"),
             "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
-                         "traffic": None, "algorithmic_bytes": dbytes},
+                         "traffic": recorded_traffic("decode"),
+                         "algorithmic_bytes": dbytes},
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth)
