@@ -22,9 +22,6 @@ constexpr int kVersion = 100;  // 0.1.0
 constexpr int kChunk = 64;     // tokens per chunk inside the prefill kernels
 constexpr int kTargetWorkgroups = 256;  // MI355X compute units
 constexpr int64_t kMinSegChunks = 8;    // shortest default segment (chunks)
-// With at most this many segments per head, each output workgroup adds up
-// its predecessors' segment sums itself; with more, a scan kernel runs.
-constexpr int kDirectPrefixMax = 8;
 // A segment's q/k/v bytes must fit one buffer descriptor (31-bit range).
 constexpr int64_t kMaxSegBytes = ((int64_t)1 << 31) - 4096;
 constexpr int64_t kMaxElems = (int64_t)1 << 46;

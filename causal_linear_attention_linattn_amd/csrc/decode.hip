@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
       n.w += red[w][tid].w;
     }
     const float den = dred[0] + dred[1] + dred[2] + dred[3];
-    const float rd = 1.0f / den;
+    const float rd = fast_rcp(den);
     T* yp = y + (size_t)bh * DV + 4 * tid;
     if constexpr (sizeof(T) == 2) {
       *reinterpret_cast<uint2*>(yp) =

@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "shapes.hpp"
 
 namespace linattn {
@@ -19,6 +21,8 @@ typedef uint16_t bf16_t;  // bf16 storage: raw bit pattern
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kInvSqrt2 = 0.70710678118654752440f;
 constexpr float kSqrt2 = 1.41421356237309504880f;
@@ -75,8 +79,20 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r,
       uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
 }
 
+// elu(x) + 1 without a compare: exp(x) >= 1 + x for every x (convexity),
+// with equality only at 0, and exp(-|x|) <= 1 < 1 + x for x > 0, so
+//   phi(x) = max(1 + x, exp(-|x|))
+// picks 1 + x for x > 0 and exp(x) for x <= 0.  One multiply, one v_exp_f32
+// (2^t, the |.| and minus are free operand modifiers), one add, one max.
+constexpr float kLog2e = 1.44269504088896340736f;
+
 __device__ __forceinline__ float phi_elu1(float x) {
-  return x > 0.0f ? x + 1.0f : __expf(x);
+  return fmaxf(x + 1.0f, __builtin_amdgcn_exp2f(-fabsf(x * kLog2e)));
+}
+
+// 1 / x in one v_rcp_f32 (1 ulp): normalisers only.
+__device__ __forceinline__ float fast_rcp(float x) {
+  return __builtin_amdgcn_rcpf(x);
 }
 
 // ---------------------------------------------------------------------------

@@ -67,11 +67,12 @@ struct PrefillShape : StateShape<MAP, DK, DV> {
   static constexpr int NKBS = (DK + 31) / 32;  // K blocks of the scores
 };
 
-// Chunks in the register prefetch ring of the chunk walker (P - 1 chunks in
-// flight while one is computed): the light segment-sum pass affords three
-// stages, the output pass two.
+// Chunks in the register prefetch ring of the chunk walker (chunks c + 2 ..
+// c + P are in flight while c is computed): the light segment-sum pass
+// affords a deeper ring than the output pass.  Even, so that one unrolled
+// trip covers the ring and the two LDS copies.
 template <bool OUT>
-constexpr int kRing = OUT ? 2 : 3;
+constexpr int kRing = OUT ? 2 : 4;
 
 // Internal feature row -> exported row (or -1 for padding) and the factor
 // that converts an exported value into the internal one.
@@ -156,8 +157,19 @@ struct RowTile {
 // y for the segment starting from its prefix state.
 //
 // Global loads are raw buffer loads whose range is the segment itself, so
-// rows past the segment end (or past N) read as zero without a branch.  The
-// next P - 1 chunks are in flight in registers while one chunk is computed.
+// rows past the segment end (or past N) read as zero without a branch, and
+// y is written with range-checked buffer stores.  Every LDS tile (and the
+// LDS copy of the state) exists twice: chunk c is computed from copy c % 2
+// while chunk c + 1 is staged into the other, so one barrier per chunk
+// suffices and the staging arithmetic of c + 1 can overlap the matrix work
+// of c.  Chunks c + 2 .. c + P are in flight in a register ring meanwhile.
+//
+// Tokens past the segment end need no masking: they read k = 0 and v = 0,
+// so they add nothing to the value columns of the state and exactly phi(0)
+// each to its z column, which is subtracted once after the walk; a valid
+// query never attends to them (causality), and their own y rows are outside
+// the store range.  Only chunks after them see the inflated z, and those
+// produce no output.
 //
 // Operands contracted over tokens (phi(K)^T and V' in the state update, V'^T
 // in the within-chunk product) need 8 consecutive tokens per lane.  bf16
@@ -173,6 +185,14 @@ struct Stage {
   uint4 q[SH::NQU];
 };
 
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 template <int MAP, typename T, int DK, int DV, bool OUT>
 __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   using SH = PrefillShape<MAP, T, DK, DV>;
@@ -182,6 +202,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   constexpr int C = SH::C, NCT = SH::NCT, NRT = SH::NRT, NKB = SH::NKB;
   constexpr int KS = SH::KS, CS = SH::CS, PS = SH::PS, EPU = SH::EPU;
   constexpr int P = kRing<OUT>;
+  static_assert(P % 2 == 0, "one unrolled trip covers the ring and both LDS copies");
   constexpr uint32_t ES = sizeof(T);
   constexpr uint32_t kOOB = 0x7ffffff0u;  // an offset no segment reaches
   using RTK = RowTile<DK>;
@@ -190,18 +211,32 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 
   // sK: rows of phi(K) (ELU1) or k (TAYLOR2); needed by the output kernel
   // for the scores and, for bf16 ELU1, by both kernels as the transposed
-  // source of phi(K)^T.  sKT: K transposed (float, and TAYLOR2).
+  // source of phi(K)^T.  sKT: K transposed (float, and TAYLOR2).  sS: the
+  // state S'^T in the MFMA operand precision, column-major; two copies
+  // unless that does not fit next to the tiles (float TAYLOR2).
   constexpr bool kNeedK = OUT || (BF && MAP == MAP_ELU1);
   constexpr bool kNeedKT = !(BF && MAP == MAP_ELU1);
-  constexpr int K_EL = BF ? C * RTK::STRIDE : C * KS;
+  constexpr int K_EL = kNeedK ? (BF ? C * RTK::STRIDE : C * KS) : EPU;
+  constexpr int KT_EL = kNeedKT ? DK * CS : EPU;
   constexpr int V_EL = BF ? C * RTV::STRIDE : DV * CS;
-  __shared__ __align__(16) T sK[kNeedK ? K_EL : EPU];
-  __shared__ __align__(16) T sKT[kNeedKT ? DK * CS : EPU];
-  __shared__ __align__(16) T sV[V_EL];
-  __shared__ __align__(16) T sS[OUT ? SH::NCOL * PS : EPU];
+  constexpr int S_EL = OUT ? SH::NCOL * PS : EPU;
+  constexpr int kTileBytes = 2 * (K_EL + KT_EL + V_EL) * (int)sizeof(T);
+  constexpr int NSB = kTileBytes + 2 * S_EL * (int)sizeof(T) <= 160 * 1024 ? 2 : 1;
+  __shared__ __align__(16) T sK0[K_EL];
+  __shared__ __align__(16) T sK1[K_EL];
+  __shared__ __align__(16) T sKT0[KT_EL];
+  __shared__ __align__(16) T sKT1[KT_EL];
+  __shared__ __align__(16) T sV0[V_EL];
+  __shared__ __align__(16) T sV1[V_EL];
+  __shared__ __align__(16) T sS0[S_EL];
+  __shared__ __align__(16) T sS1[NSB == 2 ? S_EL : EPU];
+  auto sK = [&](int b) __attribute__((always_inline)) { return b ? sK1 : sK0; };
+  auto sKT = [&](int b) __attribute__((always_inline)) { return b ? sKT1 : sKT0; };
+  auto sV = [&](int b) __attribute__((always_inline)) { return b ? sV1 : sV0; };
+  auto sS = [&](int b) __attribute__((always_inline)) { return (NSB == 2 && b) ? sS1 : sS0; };
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;  // wave-uniform, 0..3
   const int lane = tid & 63;
   const int i16 = lane & 15;
   const int g = lane >> 4;
@@ -222,6 +257,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   const auto rq = make_rsrc(qg, (uint32_t)ntok * DK * ES);
   const auto rk = make_rsrc(kg, (uint32_t)ntok * DK * ES);
   const auto rv = make_rsrc(vg, (uint32_t)ntok * DV * ES);
+  T* yg = OUT ? reinterpret_cast<T*>(a.y) + ((size_t)bh * N + tok_begin) * DV : nullptr;
+  const auto ry = make_rsrc(yg, OUT ? (uint32_t)ntok * DV * ES : 0u);
 
   // ------------------------------------------------------------ state ----
   f32x4_t Sacc[SH::MAXRT][NCT];
@@ -237,19 +274,34 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
           const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
               a.ws + ((size_t)bh * a.nseg + seg) * SH::SLOT);
           s = p[(rt * NCT + ct) * 64 + lane];
-        } else {
-          if (a.S_in != nullptr)
-            s = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, bh, rt, ct, lane);
-          // few segments: add the sums of the preceding segments directly
-          for (int j = 1; j <= seg; ++j) {
-            const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
-                a.ws + ((size_t)bh * a.nseg + j) * SH::SLOT);
-            s += p[(rt * NCT + ct) * 64 + lane];
-          }
+        } else if (a.S_in != nullptr) {
+          s = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, bh, rt, ct, lane);
         }
       }
       Sacc[m][ct] = s;
     }
+  }
+  if (OUT && a.prefix_mode == 1 && seg > 0) {
+    // Few segments: add the sums of the preceding segments (slots 1 .. seg)
+    // directly.  The loads go through a buffer resource that covers exactly
+    // those slots, so the fixed-trip loop below issues every load at once
+    // and the slots past `seg` read as zero.  (Rows past NRT, which exist
+    // only when NRT is not a multiple of the wave count, take an
+    // out-of-range offset; those accumulators are never used.)
+    const auto rw = make_rsrc(a.ws + ((size_t)bh * a.nseg + 1) * SH::SLOT,
+                              (uint32_t)seg * SH::SLOT * 4u);
+#pragma unroll
+    for (int j = 0; j < kDirectPrefixMax - 1; ++j)
+#pragma unroll
+      for (int m = 0; m < SH::MAXRT; ++m) {
+        const int rt = w + 4 * m;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const uint32_t off = rt < NRT ? ((uint32_t)j * SH::SLOT + ((rt * NCT + ct) * 64 + lane) * 4) * 4u
+                                        : kOOB;
+          Sacc[m][ct] += __builtin_bit_cast(f32x4_t, buffer_load16(rw, off));
+        }
+      }
   }
 
   // ones column of V' (and ones row of V'^T): lane column 0 of the last tile
@@ -257,14 +309,13 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) onesv[t] = i16 == 0 ? 1.0f : 0.0f;
   const frag ones = E::make(onesv);
-
   // ------------------------------------------------- tile operand access --
   // 8 tokens (tb .. tb+7) of column c0 + i16 of a row-major bf16 tile
-  auto tokfrag_bf = [&](const T* base, int stride_el, int upr_mask, int tb, int c0) -> frag {
+  auto tokfrag_bf = [&](const T* base, int stride_el, int upr_mask, int tb, int c0) __attribute__((always_inline)) -> frag {
     if constexpr (BF) {
       const int r = tb + (i16 >> 2);
       const int col = c0 + 4 * (i16 & 3);
-      auto off = [&](int row) {
+      auto off = [&](int row) __attribute__((always_inline)) {
         return row * stride_el + 8 * ((col >> 3) ^ ((row ^ (row >> 3)) & upr_mask)) + (col & 7);
       };
       const uint2 lo = lds_read_tr4(reinterpret_cast<const uint16_t*>(base) + off(r));
@@ -277,17 +328,17 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 
   // V' / V'^T operand: lane (column i16 of tile ct, g) slot t <-> token
   // 32 jb2 + 8 g + t
-  auto v_frag = [&](int jb2, int ct) -> frag {
+  auto v_frag = [&](int b, int jb2, int ct) __attribute__((always_inline)) -> frag {
     if constexpr (BF)
-      return tokfrag_bf(sV, RTV::STRIDE, RTV::UPR - 1, 32 * jb2 + 8 * g, 16 * ct);
+      return tokfrag_bf(sV(b), RTV::STRIDE, RTV::UPR - 1, 32 * jb2 + 8 * g, 16 * ct);
     else
-      return E::load8(sV + (16 * ct + i16) * CS + 32 * jb2 + 8 * g);
+      return E::load8(sV(b) + (16 * ct + i16) * CS + 32 * jb2 + 8 * g);
   };
 
   // ---------------------------------------------------------- staging ----
   St st[P];
 
-  auto issue = [&](int c, St& s) {
+  auto issue = [&](int c, St& s) __attribute__((always_inline)) {
     const uint32_t cb = (uint32_t)c * C;  // first token of chunk c
     if constexpr (BF) {
 #pragma unroll
@@ -341,10 +392,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     }
   };
 
-  // Stage chunk c into LDS.
-  auto write_tiles = [&](int c, const St& s) {
-    const int cb = c * C;
-    const bool full = cb + C <= ntok;  // no row past the segment end
+  // Stage a chunk from its ring slot into LDS copy b.
+  auto write_tiles = [&](const St& s, int b) __attribute__((always_inline)) {
     if constexpr (BF) {
 #pragma unroll
       for (int u = 0; u < St::NK; ++u) {
@@ -354,22 +403,16 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
           if constexpr (MAP == MAP_ELU1) {
             float f[8];
             unpack16<T>(s.k[u], f);
-            if (full) {
 #pragma unroll
-              for (int e = 0; e < 8; ++e) f[e] = phi_elu1(f[e]);
-            } else {
-              const bool ok = cb + row < ntok;  // phi(0) = 1: zero the pad
-#pragma unroll
-              for (int e = 0; e < 8; ++e) f[e] = ok ? phi_elu1(f[e]) : 0.0f;
-            }
-            *reinterpret_cast<uint4*>(sK + RTK::off(row, unit)) = pack16<T>(f);
+            for (int e = 0; e < 8; ++e) f[e] = phi_elu1(f[e]);
+            *reinterpret_cast<uint4*>(sK(b) + RTK::off(row, unit)) = pack16<T>(f);
           } else {
-            if constexpr (OUT) *reinterpret_cast<uint4*>(sK + RTK::off(row, unit)) = s.k[u];
+            if constexpr (OUT) *reinterpret_cast<uint4*>(sK(b) + RTK::off(row, unit)) = s.k[u];
             const uint32_t wd[4] = {s.k[u].x, s.k[u].y, s.k[u].z, s.k[u].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              sKT[(unit * 8 + 2 * e) * CS + row] = (bf16_t)(wd[e] & 0xffffu);
-              sKT[(unit * 8 + 2 * e + 1) * CS + row] = (bf16_t)(wd[e] >> 16);
+              sKT(b)[(unit * 8 + 2 * e) * CS + row] = (bf16_t)(wd[e] & 0xffffu);
+              sKT(b)[(unit * 8 + 2 * e + 1) * CS + row] = (bf16_t)(wd[e] >> 16);
             }
           }
         }
@@ -378,7 +421,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       for (int u = 0; u < St::NV; ++u) {
         const int p = tid + u * SH::NT;
         if (SH::UV % SH::NT == 0 || p < SH::UV)
-          *reinterpret_cast<uint4*>(sV + RTV::off(p / RTV::UPR, p % RTV::UPR)) = s.v[u];
+          *reinterpret_cast<uint4*>(sV(b) + RTV::off(p / RTV::UPR, p % RTV::UPR)) = s.v[u];
       }
     } else {
 #pragma unroll
@@ -391,19 +434,18 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
           unpack16<T>(s.k[2 * u], f0);
           unpack16<T>(s.k[2 * u + 1], f1);
           if constexpr (MAP == MAP_ELU1) {
-            const bool ok0 = cb + r0 < ntok, ok1 = cb + r0 + 1 < ntok;
 #pragma unroll
             for (int e = 0; e < EPU; ++e) {
-              f0[e] = ok0 ? phi_elu1(f0[e]) : 0.0f;
-              f1[e] = ok1 ? phi_elu1(f1[e]) : 0.0f;
+              f0[e] = phi_elu1(f0[e]);
+              f1[e] = phi_elu1(f1[e]);
             }
           }
           if constexpr (OUT) {
-            *reinterpret_cast<uint4*>(sK + r0 * KS + e0) = pack16<T>(f0);
-            *reinterpret_cast<uint4*>(sK + (r0 + 1) * KS + e0) = pack16<T>(f1);
+            *reinterpret_cast<uint4*>(sK(b) + r0 * KS + e0) = pack16<T>(f0);
+            *reinterpret_cast<uint4*>(sK(b) + (r0 + 1) * KS + e0) = pack16<T>(f1);
           }
 #pragma unroll
-          for (int e = 0; e < EPU; ++e) store_pair(sKT + (e0 + e) * CS + r0, f0[e], f1[e]);
+          for (int e = 0; e < EPU; ++e) store_pair(sKT(b) + (e0 + e) * CS + r0, f0[e], f1[e]);
         }
       }
 #pragma unroll
@@ -416,20 +458,20 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
           unpack16<T>(s.v[2 * u], f0);
           unpack16<T>(s.v[2 * u + 1], f1);
 #pragma unroll
-          for (int e = 0; e < EPU; ++e) store_pair(sV + (e0 + e) * CS + r0, f0[e], f1[e]);
+          for (int e = 0; e < EPU; ++e) store_pair(sV(b) + (e0 + e) * CS + r0, f0[e], f1[e]);
         }
       }
     }
   };
 
-  // Query operands of the current chunk.
-  //   ELU1:    qf[kb]  = phi(q) over features 32kb + 8g + (0..7)
-  //   TAYLOR2: qv[16]  = q;  qb8[t] = q[8(g&1) + t]
-  frag qf[MAP == MAP_ELU1 && OUT ? NKB : 1];
-  float qv[MAP == MAP_TAYLOR2 && OUT ? DK : 1];
-  float qb8[MAP == MAP_TAYLOR2 && OUT ? 8 : 1];
+  // Query operands, one set per LDS copy (the set of chunk c + 1 is formed
+  // while chunk c is computed).
+  //   ELU1:    qf[b][kb] = phi(q) over features 32kb + 8g + (0..7)
+  //   TAYLOR2: qs[b][u]  = the raw 16-byte units of q (expanded at use)
+  frag qf[2][MAP == MAP_ELU1 && OUT ? NKB : 1];
+  uint4 qs[2][MAP == MAP_TAYLOR2 && OUT ? SH::NQU : 1];
 
-  auto take_q = [&](const St& s) {
+  auto take_q = [&](const St& s, int b) __attribute__((always_inline)) {
     if constexpr (!OUT) return;
     if constexpr (MAP == MAP_ELU1) {
       constexpr int UPB = 8 / EPU;
@@ -446,48 +488,45 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
           f[t] = (32 * kb + 8 * g + t < DK) ? phi_elu1(f[t]) : 0.0f;
-        qf[kb] = E::make(f);
+        qf[b][kb] = E::make(f);
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < SH::NQU; ++u) {
-        float part[EPU];
-        unpack16<T>(s.q[u], part);
-#pragma unroll
-        for (int e = 0; e < EPU; ++e) qv[u * EPU + e] = part[e];
-      }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) qb8[t] = (g & 1) ? qv[8 + t] : qv[t];
+      for (int u = 0; u < SH::NQU; ++u) qs[b][u] = s.q[u];
     }
   };
 
+  // TAYLOR2 query of the current chunk as floats: qv[16] = q,
+  // qb8[t] = q[8 (g & 1) + t]
+  float qv[MAP == MAP_TAYLOR2 && OUT ? DK : 1];
+  float qb8[MAP == MAP_TAYLOR2 && OUT ? 8 : 1];
+
   // phi(K)^T operand for state row tile rt, key block jb2: lane (rho = i16,
   // g) slot t <-> feature 16 rt + rho, token 32 jb2 + 8 g + t.
-  auto kt_frag = [&](int rt, int jb2, int nvalid) -> frag {
+  auto kt_frag = [&](int b, int rt, int jb2) __attribute__((always_inline)) -> frag {
     const int col = 32 * jb2 + 8 * g;
     if constexpr (MAP == MAP_ELU1) {
       if (16 * rt >= DK) return E::zero();
       if constexpr (BF)
-        return tokfrag_bf(sK, RTK::STRIDE, RTK::UPR - 1, col, 16 * rt);
+        return tokfrag_bf(sK(b), RTK::STRIDE, RTK::UPR - 1, col, 16 * rt);
       else
-        return E::load8(sKT + (16 * rt + i16) * CS + col);
+        return E::load8(sKT(b) + (16 * rt + i16) * CS + col);
     } else {
       float f[8];
       if (rt < 16) {
         float fa[8], fb[8];
-        E::load8f(sKT + rt * CS + col, fa);
-        E::load8f(sKT + i16 * CS + col, fb);
+        E::load8f(sKT(b) + rt * CS + col, fa);
+        E::load8f(sKT(b) + i16 * CS + col, fb);
 #pragma unroll
         for (int t = 0; t < 8; ++t) f[t] = fa[t] * fb[t];
       } else if (rt == 16) {
         float fb[8];
-        E::load8f(sKT + (i16 == 0 ? 0 : i16 - 1) * CS + col, fb);
+        E::load8f(sKT(b) + (i16 == 0 ? 0 : i16 - 1) * CS + col, fb);
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-          f[t] = i16 == 0 ? (col + t < nvalid ? 1.0f : 0.0f) : fb[t];
+        for (int t = 0; t < 8; ++t) f[t] = i16 == 0 ? 1.0f : fb[t];
       } else {
         float fb[8];
-        E::load8f(sKT + 15 * CS + col, fb);
+        E::load8f(sKT(b) + 15 * CS + col, fb);
 #pragma unroll
         for (int t = 0; t < 8; ++t) f[t] = i16 == 0 ? fb[t] : 0.0f;
       }
@@ -496,20 +535,20 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   };
 
   // key rows for the scores: lane (key jt, g) slot t <-> feature 32 kbs + 8 g + t
-  auto k_rows = [&](int jt, int kbs) -> frag {
+  auto k_rows = [&](int b, int jt, int kbs) __attribute__((always_inline)) -> frag {
     const int f0 = 32 * kbs + 8 * g;
     if (f0 >= DK) return E::zero();
     if constexpr (BF)
-      return E::load8(sK + RTK::off(jt, f0 >> 3));
+      return E::load8(sK(b) + RTK::off(jt, f0 >> 3));
     else
-      return E::load8(sK + jt * KS + f0);
+      return E::load8(sK(b) + jt * KS + f0);
   };
 
   // phi(Q) operand for feature block kb: lane (query i16, g) slot t <->
   // feature 32 kb + 8 g + t.
-  auto q_frag = [&](int kb) -> frag {
+  auto q_frag = [&](int b, int kb) __attribute__((always_inline)) -> frag {
     if constexpr (MAP == MAP_ELU1) {
-      return qf[kb < NKB ? kb : 0];
+      return qf[b][kb < NKB ? kb : 0];
     } else {
       float f[8];
       if (kb < 8) {
@@ -529,15 +568,15 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     }
   };
 
-  // Write this wave's state tiles into the LDS copy (column-major S'^T).
-  auto publish_state = [&]() {
+  // Write this wave's state tiles into LDS copy b (column-major S'^T).
+  auto publish_state = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < SH::MAXRT; ++m) {
       const int rt = w + 4 * m;
       if (rt >= NRT) continue;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        T* p = sS + (16 * ct + i16) * PS + 16 * rt + 4 * g;
+        T* p = sS(b) + (16 * ct + i16) * PS + 16 * rt + 4 * g;
         const f32x4_t s = Sacc[m][ct];
         if constexpr (BF) {
           *reinterpret_cast<uint2*>(p) =
@@ -549,36 +588,57 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     }
   };
 
-  T* yg = OUT ? reinterpret_cast<T*>(a.y) + ((size_t)bh * N + tok_begin) * DV : nullptr;
+  // Causal mask of the within-chunk scores (the same for every chunk): lane
+  // (key slot 4h + t of block jb2, query il) keeps the score iff the key
+  // 32 jb2 + 8 g + 4 h + t is not after the query.
+  const int il = 16 * w + i16;
+  bool keep[2][8];
+#pragma unroll
+  for (int jb2 = 0; jb2 < 2; ++jb2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) keep[jb2][e] = 32 * jb2 + 8 * g + e <= il;
 
-  // One chunk: outputs (OUT) and the state update, then stage chunk c + 1
-  // from the ring slot `nx` and refill that slot with chunk c + P.
-  auto iteration = [&](int c, St& nx) {
+  // One chunk, computed from LDS copy b and query set b: stage chunk c + 1
+  // from ring slot `nx` into copy 1 - b, refill the slot with chunk c + P,
+  // then the outputs (OUT) and the state update of chunk c.
+  auto iteration = [&](int c, St& nx, auto bc) __attribute__((always_inline)) {
+    constexpr int b = decltype(bc)::value;
     const int cb = c * C;
-    const int nvalid = ntok - cb < C ? ntok - cb : C;
+
+    write_tiles(nx, 1 - b);
+    take_q(nx, 1 - b);
+    issue(c + 1 + P, nx);
 
     f32x4_t O[OUT ? NCT : 1];
     frag qraw = E::zero();
-    const int il = 16 * w + i16;
     if constexpr (OUT) {
+      if constexpr (MAP == MAP_TAYLOR2) {
+#pragma unroll
+        for (int u = 0; u < SH::NQU; ++u) {
+          float part[EPU];
+          unpack16<T>(qs[b][u], part);
+#pragma unroll
+          for (int e = 0; e < EPU; ++e) qv[u * EPU + e] = part[e];
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qb8[t] = (g & 1) ? qv[8 + t] : qv[t];
+        float f[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) f[t] = g < 2 ? qb8[t] : 0.0f;
+        qraw = E::make(f);
+      }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) O[ct] = {0.0f, 0.0f, 0.0f, 0.0f};
 
       // prefix term: O^T += S'^T phi(Q)^T
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const frag bq = q_frag(kb);
+        const frag bq = q_frag(b, kb);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const frag av = E::load8(sS + (16 * ct + i16) * PS + 32 * kb + 8 * g);
+          const frag av = E::load8(sS(b) + (16 * ct + i16) * PS + 32 * kb + 8 * g);
           E::mma(O[ct], av, bq);
         }
-      }
-      if constexpr (MAP == MAP_TAYLOR2) {
-        float f[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) f[t] = g < 2 ? qb8[t] : 0.0f;
-        qraw = E::make(f);
       }
     }
 
@@ -588,10 +648,11 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     for (int jb2 = 0; jb2 < 2; ++jb2) {
       frag vf[NCT - 1];
 #pragma unroll
-      for (int ct = 0; ct < NCT - 1; ++ct) vf[ct] = v_frag(jb2, ct);
+      for (int ct = 0; ct < NCT - 1; ++ct) vf[ct] = v_frag(b, jb2, ct);
 
-      if (OUT && 32 * jb2 <= 16 * w + 15) {
-        // within-chunk term: scores^T for keys <= this wave's queries
+      if constexpr (OUT) {
+        // within-chunk term: scores^T of this key block against the wave's
+        // queries (key blocks wholly after them come out fully masked)
         f32x4_t sc[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -600,13 +661,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
           for (int kbs = 0; kbs < SH::NKBS; ++kbs) {
             frag bq;
-            if constexpr (MAP == MAP_ELU1) bq = q_frag(kbs); else bq = qraw;
-            E::mma(sc[h], k_rows(jt, kbs), bq);
+            if constexpr (MAP == MAP_ELU1) bq = q_frag(b, kbs); else bq = qraw;
+            E::mma(sc[h], k_rows(b, jt, kbs), bq);
           }
         }
-        // keys of this block are all <= every query of the wave unless the
-        // block reaches past the wave's first query
-        const bool diag = 32 * jb2 + 31 > 16 * w;
         float f[8];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -615,21 +673,12 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
             const float sv = sc[h][t];
             float val;
             if constexpr (MAP == MAP_ELU1) val = sv; else val = 1.0f + sv + 0.5f * sv * sv;
-            f[4 * h + t] = val;
+            f[4 * h + t] = keep[jb2][4 * h + t] ? val : 0.0f;
           }
-        if (diag) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              if (32 * jb2 + 8 * g + 4 * h + t > il) f[4 * h + t] = 0.0f;
-        }
         const frag bA = E::make(f);
-        if constexpr (OUT) {
 #pragma unroll
-          for (int ct = 0; ct < NCT - 1; ++ct) E::mma(O[ct], vf[ct], bA);
-          E::mma(O[NCT - 1], ones, bA);
-        }
+        for (int ct = 0; ct < NCT - 1; ++ct) E::mma(O[ct], vf[ct], bA);
+        E::mma(O[NCT - 1], ones, bA);
       }
 
       // state update: S' += phi(K)^T V' for this wave's row tiles
@@ -637,7 +686,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       for (int m = 0; m < SH::MAXRT; ++m) {
         const int rt = w + 4 * m;
         if (rt >= NRT) continue;
-        const frag ak = kt_frag(rt, jb2, nvalid);
+        const frag ak = kt_frag(b, rt, jb2);
 #pragma unroll
         for (int ct = 0; ct < NCT - 1; ++ct) E::mma(Sacc[m][ct], ak, vf[ct]);
         E::mma(Sacc[m][NCT - 1], ak, ones);
@@ -645,61 +694,71 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     }
 
     if constexpr (OUT) {
-      // normalise and write y (query il of this chunk)
+      // normalise and write y (query il of this chunk; rows past the
+      // segment end fall outside the store range)
       const float den = __shfl(O[NCT - 1][0], i16, 64);
-      const float rden = 1.0f / den;
-      if (cb + il < ntok) {
-        T* yrow = yg + (size_t)(cb + il) * DV;
+      const float rden = fast_rcp(den);
+      const uint32_t yrow = ((uint32_t)(cb + il) * DV + 4 * g) * ES;
 #pragma unroll
-        for (int ct = 0; ct < NCT - 1; ++ct) {
-          const f32x4_t o = O[ct];
-          T* p = yrow + 16 * ct + 4 * g;
-          if constexpr (BF) {
-            *reinterpret_cast<uint2*>(p) =
-                make_uint2(pack_bf16x2(o[0] * rden, o[1] * rden),
-                           pack_bf16x2(o[2] * rden, o[3] * rden));
-          } else {
-            *reinterpret_cast<float4*>(p) =
-                make_float4(o[0] * rden, o[1] * rden, o[2] * rden, o[3] * rden);
-          }
+      for (int ct = 0; ct < NCT - 1; ++ct) {
+        const f32x4_t o = O[ct];
+        const uint32_t off = yrow + 16 * ct * ES;
+        if constexpr (BF) {
+          const uint2 d = make_uint2(pack_bf16x2(o[0] * rden, o[1] * rden),
+                                     pack_bf16x2(o[2] * rden, o[3] * rden));
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, d), ry, off, 0, 0);
+        } else {
+          const uint4 d = make_uint4(__float_as_uint(o[0] * rden), __float_as_uint(o[1] * rden),
+                                     __float_as_uint(o[2] * rden), __float_as_uint(o[3] * rden));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, d), ry, off, 0, 0);
         }
       }
+      // state through chunk c for the prefix term of chunk c + 1
+      if constexpr (NSB == 1) lds_barrier();  // every wave is done with sS
+      publish_state(1 - b);
     }
-
-    lds_barrier();  // every wave is done reading the tiles and sS
-    if constexpr (OUT) publish_state();
-    // Stage chunk c + 1 even past the end: its loads are out of range and
-    // read zeros, and nothing reads those tiles.  An unconditional staging
-    // step keeps the compiler's count of loads in flight exact.
-    write_tiles(c + 1, nx);
-    take_q(nx);
-    issue(c + 1 + P, nx);
-    // keep the loads here: without this fence the compiler sinks them to
-    // their use P - 1 chunks later, which leaves nothing in flight
-    asm volatile("" ::: "memory");
     lds_barrier();
   };
 
   // ------------------------------------------------------------ prologue --
 #pragma unroll
   for (int s = 0; s < P; ++s) issue(s, st[s]);
-  asm volatile("" ::: "memory");
-  if constexpr (OUT) publish_state();
-  write_tiles(0, st[0]);
-  take_q(st[0]);
+  if constexpr (OUT) publish_state(0);
+  write_tiles(st[0], 0);
+  take_q(st[0], 0);
   issue(P, st[0]);
-  asm volatile("" ::: "memory");
   lds_barrier();
 
-  // Chunk c is staged from ring slot c % P; unrolling by P keeps every ring
-  // index a compile-time constant.  The loop runs whole trips of P chunks
-  // with no branch between the copies; chunks past the segment end are
-  // inert (their loads are out of range and read zeros, phi(K) and the
-  // constant Taylor feature are masked to zero there, and no y row is
-  // written), so at most P - 1 empty chunks are walked at the end.
+  // Chunk c is staged from ring slot c % P into LDS copy c % 2; one trip of
+  // P chunks keeps every ring index and copy index a compile-time constant.
+  // The loop runs whole trips with no branch between the copies; chunks
+  // past the segment end are inert (their loads are out of range and read
+  // zeros, their ones column is masked, and no y row of theirs is in the
+  // store range), so at most P - 1 empty chunks are walked at the end.
   for (int c0 = 0; c0 < nchunks; c0 += P) {
+    static_for<0, P>([&](auto s) __attribute__((always_inline)) {
+      constexpr int S = decltype(s)::value;
+      iteration(c0 + S, st[(S + 1) % P], std::integral_constant<int, S % 2>{});
+    });
+  }
+
+  // Every token walked past the segment end (the tail of the last chunk and
+  // the empty chunks of the last trip) read k = 0 and v = 0: it added
+  // nothing to the value columns and phi(0) to the z column.  Take that
+  // back: phi(0) is 1 in every ELU1 feature, and in the TAYLOR2 constant
+  // feature (internal row 256) only.
+  {
+    const float n_pad = (float)(((nchunks + P - 1) / P) * P * C - ntok);
 #pragma unroll
-    for (int s = 0; s < P; ++s) iteration(c0 + s, st[(s + 1) % P]);
+    for (int m = 0; m < SH::MAXRT; ++m) {
+      const int rt = w + 4 * m;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int row = 16 * rt + 4 * g + t;
+        const bool unit_feature = MAP == MAP_ELU1 ? row < DK : row == 256;
+        if (i16 == 0 && unit_feature) Sacc[m][NCT - 1][t] -= n_pad;
+      }
+    }
   }
 
   // ------------------------------------------------------------ epilogue --

@@ -9,6 +9,11 @@ namespace linattn {
 
 enum { MAP_ELU1 = 0, MAP_TAYLOR2 = 1 };
 
+// Most segments per head for which each output workgroup adds up the sums
+// of its preceding segments itself (prefix_mode 1); beyond it a scan kernel
+// forms the prefixes (prefix_mode 2).
+constexpr int kDirectPrefixMax = 8;
+
 struct PrefillArgs {
   const void* q;
   const void* k;
