@@ -807,9 +807,19 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(PrefillArgs a) {
   }
   f32x4_t* p = reinterpret_cast<f32x4_t*>(a.ws + (size_t)bh * a.nseg * SS::SLOT) + e4;
   p[0] = run;
-  for (int s = 1; s < a.nseg; ++s) {
-    run += p[(size_t)s * Q];
-    p[(size_t)s * Q] = run;
+  // batches of 16 slots: all loads of a batch are in flight at once
+  constexpr int kB = 16;
+  for (int s0 = 1; s0 < a.nseg; s0 += kB) {
+    f32x4_t t[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+      if (s0 + j < a.nseg) t[j] = p[(size_t)(s0 + j) * Q];
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+      if (s0 + j < a.nseg) {
+        run += t[j];
+        p[(size_t)(s0 + j) * Q] = run;
+      }
   }
 }
 
