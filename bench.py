@@ -11,7 +11,9 @@ per step, all heads).  The same JSON line carries:
                 (D = 273), state seeded by the library's own prefill over a
                 1024-token prefix, 128 steps; steps/s and its HBM roofline
                 (algorithmic bytes: state read + written, q, k, v, y);
-  cpu_baseline  the float64 oracle on the host, on a bounded sample.
+  cpu_baseline  the float64 oracle on the host, on a bounded sample;
+  other_configs the Taylor-2 and 64K-token prefills, and an N sweep (4K to
+                64K tokens) showing time linear in N.
 Inputs are seeded synthetic Gaussians (synth.py); nothing is read from disk.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -64,16 +66,19 @@ def decode_step_bytes(cfg):
                  + (2 * cfg["d_k"] + 2 * cfg["d_v"]) * es)
 
 
-def time_prefill(args, ops, synth, torch):
-    cfg = synth.WORKLOADS[PREFILL]
+def time_prefill(args, ops, synth, torch, name=PREFILL, override=None, steps=None):
+    cfg = dict(synth.WORKLOADS[name])
+    cfg.update(override or {})
     dev = "cuda:0"
-    q, k, v = synth.workload_inputs(PREFILL, seed=0)
+    q, k, v = synth.workload_inputs(name, seed=0, **(override or {}))
     base = [ops.to_device(x, dev) for x in (q, k, v)]
     set_bytes = prefill_bytes(cfg)
     nsets = max(2, -(-ROTATE_BYTES // set_bytes))
     L = ops.load_library()
     B, H, N, dk, dv = cfg["B"], cfg["H"], cfg["N"], cfg["d_k"], cfg["d_v"]
-    nws = ops.workspace_bytes("elu1", torch.bfloat16, B, H, N, dk, dv, 0)
+    fmap = cfg["fmap"]
+    tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    nws = ops.workspace_bytes(fmap, tdt, B, H, N, dk, dv, 0)
     stream = ops._stream(base[0])
     sets = []
     for i in range(nsets):
@@ -81,7 +86,8 @@ def time_prefill(args, ops, synth, torch):
         y = torch.empty_like(vd)
         ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
         sets.append((qd, kd, vd, y, ws))
-    calls = [(ops.MAPS["elu1"], 1, B, H, N, dk, dv, ops._ptr(s[0]), ops._ptr(s[1]),
+    dcode = 1 if cfg["dtype"] == "bf16" else 0
+    calls = [(ops.MAPS[fmap], dcode, B, H, N, dk, dv, ops._ptr(s[0]), ops._ptr(s[1]),
               ops._ptr(s[2]), ops._ptr(s[3]), None, None, None, None, 0,
               ops._ptr(s[4]), nws, stream) for s in sets]
 
@@ -90,18 +96,28 @@ def time_prefill(args, ops, synth, torch):
         if rc:
             raise RuntimeError(f"linattn_prefill returned {rc}")
 
+    nsteps = args.steps if steps is None else steps
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record()
-    for i in range(args.steps):
+    for i in range(nsteps):
         step(i)
     ev1.record()
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = ev0.elapsed_time(ev1) / nsteps
+    del sets, base
     return cfg, ms, nsets
+
+
+def prefill_record(cfg, ms):
+    """tokens/s and the HBM roofline fraction of one timed prefill config."""
+    gbs = prefill_bytes(cfg) / (ms * 1e-3) / 1e9
+    return {"us_per_call": ms * 1e3, "tokens_per_s": cfg["B"] * cfg["N"] / (ms * 1e-3),
+            "hbm_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "mfma_frac": prefill_flops(cfg) / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
 def time_decode(args, ops, synth, torch):
@@ -137,8 +153,26 @@ def time_decode(args, ops, synth, torch):
     ev1.record()
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / (reps * T)
+
+    # the same 128 steps captured in one HIP graph (launches replayed by the
+    # runtime); per-step time = graph time / 128
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = ops._stream(S)
+        for c in calls:
+            rc = L.linattn_decode_step(*c[:-1], cap)
+            if rc:
+                raise RuntimeError(f"linattn_decode_step returned {rc}")
+    g.replay()
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_graph = ev0.elapsed_time(ev1) / (reps * T)
     ok = bool(torch.isfinite(y.float()).all().item())
-    return cfg, ms_step, ok
+    return cfg, ms_step, ok, ms_graph
 
 
 def csrc_digest():
@@ -247,6 +281,8 @@ def main():
                     help="128-step generations timed for the decode figure")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the Taylor / long-sequence prefills and the N sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy used to scale HBM counters")
     args = ap.parse_args()
@@ -275,6 +311,22 @@ def main():
         return
 
     cfg, ms, nsets = time_prefill(args, ops, synth, torch)
+    others = {}
+    if not args.no_other_configs:
+        # the other prefill configurations (not the headline line)
+        for name in ("based_taylor2_bf16", "long_elu1_bf16"):
+            c2, ms2, _ = time_prefill(args, ops, synth, torch, name=name, steps=50)
+            others[name] = dict(prefill_record(c2, ms2),
+                                workload=(f"prefill {c2['fmap']} B={c2['B']} H={c2['H']} "
+                                          f"N={c2['N']} d_k={c2['d_k']} d_v={c2['d_v']} "
+                                          f"{c2['dtype']}"))
+        # linear in N: ELU1 bf16, B=1 H=8 d=64, N from 4K to 64K
+        sweep = []
+        for n in (4096, 8192, 16384, 32768, 65536):
+            c3, ms3, _ = time_prefill(args, ops, synth, torch, name="long_elu1_bf16",
+                                      override={"N": n}, steps=50)
+            sweep.append(dict(N=n, **prefill_record(c3, ms3)))
+        others["n_sweep_elu1_b1h8_d64_bf16"] = sweep
     tokens = cfg["B"] * cfg["N"]
     nbytes = prefill_bytes(cfg)
     flops = prefill_flops(cfg)
@@ -309,8 +361,10 @@ def main():
             "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         },
     }
+    if others:
+        out["other_configs"] = others
     if not args.no_decode:
-        dcfg, dms, finite = time_decode(args, ops, synth, torch)
+        dcfg, dms, finite, dms_graph = time_decode(args, ops, synth, torch)
         dbytes = decode_step_bytes(dcfg)
         dgbs = dbytes / (dms * 1e-3) / 1e9
         out["decode"] = {
@@ -324,6 +378,9 @@ def main():
                          "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
                          "traffic": recorded_traffic("decode"),
                          "algorithmic_bytes": dbytes},
+            "graph": {"ms_per_step": dms_graph, "steps_per_s": 1e3 / dms_graph,
+                      "hbm_frac": dbytes / (dms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "note": "the 128 steps captured in one HIP graph and replayed"},
         }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth)

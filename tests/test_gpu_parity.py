@@ -206,6 +206,43 @@ def test_decode_from_oracle_state(fmap, d_k, d_v, dtype):
     assert state_err(ops.to_numpy64(zd)[..., None], z_ref[..., None]) <= 1e-4
 
 
+@pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64)])
+def test_decode_graph_replays_match_eager(fmap, d_k, d_v):
+    """Eight decode steps captured in one HIP graph: every replay (state
+    reset between replays by an eager copy, other eager work in between)
+    gives bit-identical outputs and state to the same steps run eagerly."""
+    _log(f"decode graph replays {fmap}")
+    B, H, P, T = 3, 4, 64, 8
+    q, k, v = synth.draw_qkv(B, H, P, d_k, d_v, seed=31, dtype="bf16")
+    qs, ks, vs = synth.draw_qkv(B, H, T, d_k, d_v, seed=31, dtype="bf16", stream=1)
+    S0, z0 = oracle.final_state(k.f64(), v.f64(), fmap)
+    S0d = torch.from_numpy(S0.astype(np.float32)).to(DEV)
+    z0d = torch.from_numpy(z0.astype(np.float32)).to(DEV)
+    step = [ops.to_device(x, DEV).permute(2, 0, 1, 3).contiguous() for x in (qs, ks, vs)]
+
+    S_e, z_e = S0d.clone(), z0d.clone()
+    y_e = [ops.decode_step(step[0][t], step[1][t], step[2][t], S_e, z_e, fmap)
+           for t in range(T)]
+    torch.cuda.synchronize()
+
+    S_g, z_g = S0d.clone(), z0d.clone()
+    y_g = torch.empty((T, B, H, d_v), dtype=torch.bfloat16, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(T):
+            ops.decode_step(step[0][t], step[1][t], step[2][t], S_g, z_g, fmap, out=y_g[t])
+    for r in range(3):
+        S_g.copy_(S0d)
+        z_g.copy_(z0d)
+        junk = (S0d * 2.0).sum()  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for t in range(T):
+            assert torch.equal(y_g[t], y_e[t]), (r, t)
+        assert torch.equal(S_g, S_e) and torch.equal(z_g, z_e), r
+
+
 # ------------------------------------------------------ full-size configs --
 def _sampled_rows(n, rng, count=32):
     rows = set([0, n - 1]) | set(rng.integers(0, n, size=count).tolist())
