@@ -642,6 +642,20 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       }
     }
 
+    // Scheduling hint: interleave the staging arithmetic of chunk c + 1 (phi
+    // of k and q, independent of this chunk's products) with this chunk's
+    // first MFMAs, eight VALU instructions after each MFMA, so that the
+    // matrix unit is not idle while the wave computes phi.  Measured on the
+    // ELU1 shapes only; the TAYLOR2 schedule is left to the compiler.
+    if constexpr (MAP == MAP_ELU1) {
+      constexpr int kInterleave = OUT ? NKB * NCT : SH::MAXRT * NCT * 2;
+#pragma unroll
+      for (int i = 0; i < kInterleave; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight VALU
+      }
+    }
+
     // Per 32-token key block: the V' operands serve both the within-chunk
     // product (A-operand, V'^T) and the state update (B-operand, V').
 #pragma unroll
