@@ -13,7 +13,10 @@ per step, all heads).  The same JSON line carries:
                 (algorithmic bytes: state read + written, q, k, v, y);
   cpu_baseline  the float64 oracle on the host, on a bounded sample;
   other_configs the Taylor-2 and 64K-token prefills, and an N sweep (4K to
-                64K tokens) showing time linear in N.
+                64K tokens) showing time linear in N;
+  roofline.intra_chunk_mfma_probe
+                the MFMA rate of the prefill's within-chunk device code on
+                LDS-resident tiles, looped (liblinattn_probe.so).
 Inputs are seeded synthetic Gaussians (synth.py); nothing is read from disk.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -175,6 +178,42 @@ def time_decode(args, ops, synth, torch):
     return cfg, ms_step, ok, ms_graph
 
 
+def intra_mfma_probe(torch, iters=2000):
+    """MFMA rate of the prefill's within-chunk device code on LDS-resident
+    bf16 tiles, looped (liblinattn_probe.so): executed MFMA flops / time."""
+    import ctypes
+
+    path = os.path.join(ROOT, "causal_linear_attention_linattn_amd", "liblinattn_probe.so")
+    if not os.path.exists(path):
+        return None
+    P = ctypes.CDLL(path)
+    P.linattn_probe_intra_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    P.linattn_probe_intra_mfma_per_iter.argtypes = [ctypes.c_int]
+    out = {}
+    for name, m in (("elu1_d64", 0), ("taylor2_d16_dv64", 1)):
+        per_iter = P.linattn_probe_intra_mfma_per_iter(m)
+        for per_cu in (1, 2, 3):
+            wgs = 256 * per_cu
+            sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            args = (m, iters, wgs, ctypes.c_void_p(sink.data_ptr()), st)
+            if P.linattn_probe_intra_mfma(*args):
+                raise RuntimeError("intra-chunk probe launch failed")
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            P.linattn_probe_intra_mfma(*args)
+            ev1.record()
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1)
+            flops = wgs * 4 * iters * per_iter * 2 * 16 * 16 * 32
+            tf = flops / (ms * 1e-3) / 1e12
+            out[f"{name}_{per_cu}wg_per_cu"] = {"tflops": tf,
+                                                "frac_of_peak": tf / MFMA_BF16_PEAK_TFLOPS}
+    return out
+
+
 def csrc_digest():
     """Hash of the HIP sources; a traffic figure is valid only for this hash."""
     import hashlib
@@ -182,7 +221,10 @@ def csrc_digest():
     d = hashlib.sha256()
     csrc = os.path.join(ROOT, "causal_linear_attention_linattn_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+        path = os.path.join(csrc, name)
+        if not os.path.isfile(path):
+            continue  # the measurement probe (csrc/probe) is not the product
+        with open(path, "rb") as f:
             d.update(name.encode() + b"\0" + f.read())
     return d.hexdigest()[:16]
 
@@ -363,6 +405,10 @@ def main():
     }
     if others:
         out["other_configs"] = others
+    if not args.no_other_configs:
+        probe = intra_mfma_probe(torch)
+        if probe:
+            out["roofline"]["intra_chunk_mfma_probe"] = probe
     if not args.no_decode:
         dcfg, dms, finite, dms_graph = time_decode(args, ops, synth, torch)
         dbytes = decode_step_bytes(dcfg)

@@ -176,6 +176,91 @@ struct RowTile {
 // tiles are kept row-major and read with the LDS transpose read; float
 // tiles are stored transposed (two tokens per store).
 // ---------------------------------------------------------------------------
+// Operand reads from the chunk tiles in LDS and the within-chunk product of
+// one 16-query tile against one 32-token key block ([SLA] Knowl 5: the
+// masked quadratic term of a tile).  Shared by the chunk walker and the
+// looped LDS-resident throughput probe of the intra-chunk products.
+template <int MAP, typename T, int DK, int DV>
+struct ChunkTiles {
+  using SH = PrefillShape<MAP, T, DK, DV>;
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  static constexpr bool BF = sizeof(T) == 2;
+  static constexpr int NCT = SH::NCT;
+  using RTK = RowTile<DK>;
+  using RTV = RowTile<DV>;
+
+  // 8 tokens (tb .. tb+7) of column c0 + i16 of a row-major bf16 tile
+  __device__ static __forceinline__ frag tokfrag_bf(const T* base, int stride_el, int upr_mask,
+                                                    int tb, int c0, int lane) {
+    if constexpr (BF) {
+      const int i16 = lane & 15;
+      const int r = tb + (i16 >> 2);
+      const int col = c0 + 4 * (i16 & 3);
+      auto off = [&](int row) __attribute__((always_inline)) {
+        return row * stride_el + 8 * ((col >> 3) ^ ((row ^ (row >> 3)) & upr_mask)) + (col & 7);
+      };
+      const uint2 lo = lds_read_tr4(reinterpret_cast<const uint16_t*>(base) + off(r));
+      const uint2 hi = lds_read_tr4(reinterpret_cast<const uint16_t*>(base) + off(r + 4));
+      return __builtin_bit_cast(frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    } else {
+      return E::zero();
+    }
+  }
+
+  // V' / V'^T operand: lane (column i16 of tile ct, g) slot t <-> token
+  // 32 jb2 + 8 g + t
+  __device__ static __forceinline__ frag v_frag(const T* sV, int jb2, int ct, int lane) {
+    const int i16 = lane & 15, g = lane >> 4;
+    if constexpr (BF)
+      return tokfrag_bf(sV, RTV::STRIDE, RTV::UPR - 1, 32 * jb2 + 8 * g, 16 * ct, lane);
+    else
+      return E::load8(sV + (16 * ct + i16) * SH::CS + 32 * jb2 + 8 * g);
+  }
+
+  // key rows for the scores: lane (key jt, g) slot t <-> feature 32 kbs + 8 g + t
+  __device__ static __forceinline__ frag k_rows(const T* sK, int jt, int kbs, int lane) {
+    const int f0 = 32 * kbs + 8 * (lane >> 4);
+    if (f0 >= DK) return E::zero();
+    if constexpr (BF)
+      return E::load8(sK + RTK::off(jt, f0 >> 3));
+    else
+      return E::load8(sK + jt * SH::KS + f0);
+  }
+
+  // O^T += V'^T A^T for key block jb2, where A^T = scores^T of the block's
+  // keys against the wave's 16 queries (operands bq), kept where keep[] is
+  // set (the causal mask); TAYLOR2 turns the raw q.k into 1 + s + s^2 / 2.
+  __device__ static __forceinline__ void within_chunk(const T* sK, const frag (&vf)[NCT - 1],
+                                                      const frag (&bq)[SH::NKBS], const bool (&keep)[8],
+                                                      const frag& ones, f32x4_t (&O)[NCT], int jb2,
+                                                      int lane) {
+    const int i16 = lane & 15;
+    f32x4_t sc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sc[h] = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int jt = 32 * jb2 + 8 * (i16 >> 2) + 4 * h + (i16 & 3);
+#pragma unroll
+      for (int kbs = 0; kbs < SH::NKBS; ++kbs) E::mma(sc[h], k_rows(sK, jt, kbs, lane), bq[kbs]);
+    }
+    float f[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float sv = sc[h][t];
+        float val;
+        if constexpr (MAP == MAP_ELU1) val = sv; else val = 1.0f + sv + 0.5f * sv * sv;
+        f[4 * h + t] = keep[4 * h + t] ? val : 0.0f;
+      }
+    const frag bA = E::make(f);
+#pragma unroll
+    for (int ct = 0; ct < NCT - 1; ++ct) E::mma(O[ct], vf[ct], bA);
+    E::mma(O[NCT - 1], ones, bA);
+  }
+};
+
 template <class SH, bool BF>
 struct Stage {
   static constexpr int NK = BF ? SH::NUK : 2 * SH::NPK;
@@ -310,29 +395,12 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   for (int t = 0; t < 8; ++t) onesv[t] = i16 == 0 ? 1.0f : 0.0f;
   const frag ones = E::make(onesv);
   // ------------------------------------------------- tile operand access --
-  // 8 tokens (tb .. tb+7) of column c0 + i16 of a row-major bf16 tile
+  using CT = ChunkTiles<MAP, T, DK, DV>;
   auto tokfrag_bf = [&](const T* base, int stride_el, int upr_mask, int tb, int c0) __attribute__((always_inline)) -> frag {
-    if constexpr (BF) {
-      const int r = tb + (i16 >> 2);
-      const int col = c0 + 4 * (i16 & 3);
-      auto off = [&](int row) __attribute__((always_inline)) {
-        return row * stride_el + 8 * ((col >> 3) ^ ((row ^ (row >> 3)) & upr_mask)) + (col & 7);
-      };
-      const uint2 lo = lds_read_tr4(reinterpret_cast<const uint16_t*>(base) + off(r));
-      const uint2 hi = lds_read_tr4(reinterpret_cast<const uint16_t*>(base) + off(r + 4));
-      return __builtin_bit_cast(frag, make_uint4(lo.x, lo.y, hi.x, hi.y));
-    } else {
-      return E::zero();
-    }
+    return CT::tokfrag_bf(base, stride_el, upr_mask, tb, c0, lane);
   };
-
-  // V' / V'^T operand: lane (column i16 of tile ct, g) slot t <-> token
-  // 32 jb2 + 8 g + t
   auto v_frag = [&](int b, int jb2, int ct) __attribute__((always_inline)) -> frag {
-    if constexpr (BF)
-      return tokfrag_bf(sV(b), RTV::STRIDE, RTV::UPR - 1, 32 * jb2 + 8 * g, 16 * ct);
-    else
-      return E::load8(sV(b) + (16 * ct + i16) * CS + 32 * jb2 + 8 * g);
+    return CT::v_frag(sV(b), jb2, ct, lane);
   };
 
   // ---------------------------------------------------------- staging ----
@@ -534,16 +602,6 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     }
   };
 
-  // key rows for the scores: lane (key jt, g) slot t <-> feature 32 kbs + 8 g + t
-  auto k_rows = [&](int b, int jt, int kbs) __attribute__((always_inline)) -> frag {
-    const int f0 = 32 * kbs + 8 * g;
-    if (f0 >= DK) return E::zero();
-    if constexpr (BF)
-      return E::load8(sK(b) + RTK::off(jt, f0 >> 3));
-    else
-      return E::load8(sK(b) + jt * KS + f0);
-  };
-
   // phi(Q) operand for feature block kb: lane (query i16, g) slot t <->
   // feature 32 kb + 8 g + t.
   auto q_frag = [&](int b, int kb) __attribute__((always_inline)) -> frag {
@@ -667,32 +725,12 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       if constexpr (OUT) {
         // within-chunk term: scores^T of this key block against the wave's
         // queries (key blocks wholly after them come out fully masked)
-        f32x4_t sc[2];
+        frag bq[SH::NKBS];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          sc[h] = {0.0f, 0.0f, 0.0f, 0.0f};
-          const int jt = 32 * jb2 + 8 * (i16 >> 2) + 4 * h + (i16 & 3);
-#pragma unroll
-          for (int kbs = 0; kbs < SH::NKBS; ++kbs) {
-            frag bq;
-            if constexpr (MAP == MAP_ELU1) bq = q_frag(b, kbs); else bq = qraw;
-            E::mma(sc[h], k_rows(b, jt, kbs), bq);
-          }
+        for (int kbs = 0; kbs < SH::NKBS; ++kbs) {
+          if constexpr (MAP == MAP_ELU1) bq[kbs] = q_frag(b, kbs); else bq[kbs] = qraw;
         }
-        float f[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float sv = sc[h][t];
-            float val;
-            if constexpr (MAP == MAP_ELU1) val = sv; else val = 1.0f + sv + 0.5f * sv * sv;
-            f[4 * h + t] = keep[jb2][4 * h + t] ? val : 0.0f;
-          }
-        const frag bA = E::make(f);
-#pragma unroll
-        for (int ct = 0; ct < NCT - 1; ++ct) E::mma(O[ct], vf[ct], bA);
-        E::mma(O[NCT - 1], ones, bA);
+        CT::within_chunk(sK(b), vf, bq, keep[jb2], ones, O, jb2, lane);
       }
 
       // state update: S' += phi(K)^T V' for this wave's row tiles
