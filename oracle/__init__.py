@@ -7,6 +7,7 @@ from .linattn_oracle import (  # noqa: F401
     ELU1,
     MAPS,
     TAYLOR2,
+    TAYLOR2_SYM,
     attention_quadratic,
     attention_recurrent,
     attention_rows,
@@ -17,4 +18,6 @@ from .linattn_oracle import (  # noqa: F401
     kernel_value,
     phi_elu1,
     phi_taylor2,
+    phi_taylor2_sym,
+    sym_pairs,
 )

@@ -26,6 +26,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
     order, feature index 1 + d + i*d + j for x_i*x_j; [SLA] Knowl 3 gives only
     the identity phi(q).phi(k) = 1 + q.k + (q.k)^2/2 and "constant,
     first-order, second-order pairwise products".
+  * The unordered-pair Taylor map ("taylor2sym") is [1, x, q_ab] with q_ab
+    = x_a x_b for a < b and x_a^2 / sqrt(2) for a = b, pairs in row-major
+    upper-triangular order; [SLA] Knowl 7 gives only its size.
   * The causal sum includes the diagonal (sum over j = 1..i, [SLA] Knowl 3).
   * No epsilon in the denominator; it is positive for both maps.
   * Generation updates the state first and then reads it ([SLA] Knowl 3
@@ -46,7 +49,8 @@ import numpy as np
 
 ELU1 = "elu1"
 TAYLOR2 = "taylor2"
-MAPS = (ELU1, TAYLOR2)
+TAYLOR2_SYM = "taylor2sym"
+MAPS = (ELU1, TAYLOR2, TAYLOR2_SYM)
 
 
 def _f64(x) -> np.ndarray:
@@ -77,11 +81,38 @@ def phi_taylor2(x) -> np.ndarray:
     return np.concatenate([ones, x, quad], axis=-1)
 
 
+def sym_pairs(d: int):
+    """Unordered pairs (a, b), a <= b, in row-major upper-triangular order:
+    (0,0), (0,1), ..., (0,d-1), (1,1), ..., (d-1,d-1)."""
+    return [(a, b) for a in range(d) for b in range(a, d)]
+
+
+def phi_taylor2_sym(x) -> np.ndarray:
+    """Second-order Taylor map on unordered pairs (reading; see header).
+
+    [SLA] Knowl 7 counts the generation state of the Taylor map as
+    (d + 1)(1 + 3d'/2 + d'^2/2) per head: constant, d' first-order and
+    d'(d' + 1)/2 second-order features, i.e. each unordered pair once.
+    Keeping phi(q).phi(k) = 1 + q.k + (q.k)^2/2 (Knowl 3) fixes the weights:
+    (q.k)^2/2 = sum_a q_a^2 k_a^2 / 2 + sum_{a<b} q_a q_b k_a k_b, so the
+    square x_a^2 carries 1/sqrt(2) and the product x_a x_b (a < b) weight 1.
+    Layout [1, x, pairs in sym_pairs order]; width 1 + d + d(d+1)/2.
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    ones = np.ones(x.shape[:-1] + (1,), dtype=np.float64)
+    quad = np.stack([x[..., a] * x[..., b] * (1.0 / math.sqrt(2.0) if a == b else 1.0)
+                     for a, b in sym_pairs(d)], axis=-1)
+    return np.concatenate([ones, x, quad], axis=-1)
+
+
 def feature_dim(fmap: str, d_k: int) -> int:
     if fmap == ELU1:
         return d_k
     if fmap == TAYLOR2:
         return 1 + d_k + d_k * d_k
+    if fmap == TAYLOR2_SYM:
+        return 1 + d_k + d_k * (d_k + 1) // 2
     raise ValueError(f"unknown feature map {fmap!r}")
 
 
@@ -90,6 +121,8 @@ def feature_map(x, fmap: str) -> np.ndarray:
         return phi_elu1(x)
     if fmap == TAYLOR2:
         return phi_taylor2(x)
+    if fmap == TAYLOR2_SYM:
+        return phi_taylor2_sym(x)
     raise ValueError(f"unknown feature map {fmap!r}")
 
 

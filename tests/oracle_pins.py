@@ -15,6 +15,9 @@ recall-throughput tradeoff" = SLA; "Transformers are RNNs ..." = TR):
   taylor_exp       the same kernel is exp's second-order Taylor polynomial:
                    |kernel - exp(s)| <= |s|^3 / 6 * exp(|s|)
   taylor_layout    hand-written feature vector for x = (1, 2, -3)
+  taylor_sym_*     the unordered-pair map: SLA Knowl 7's state size (153 at
+                   d' = 16), the Knowl 3 identity, hand-written features,
+                   and the fold relation to the ordered-pair state
   elu_torch        torch.nn.functional.elu(x) + 1 (a library routine)
   closed forms     first token, constant key, zero Taylor query, constant v,
                    linearity in v, convex hull, positivity, final state,
@@ -61,11 +64,24 @@ def _exact_kernel(fmap, qi, kj):
     return tot
 
 
+def _exact_kernel_sym(qi, kj):
+    """phi(q).phi(k) through the unordered-pair features, exactly: 1*1,
+    q_a*k_a, (q_a^2/sqrt2)(k_a^2/sqrt2) = q_a^2 k_a^2 / 2, and
+    (q_a q_b)(k_a k_b) for a < b (SLA Knowl 7 counts each pair once)."""
+    d = len(qi)
+    tot = Fraction(1)
+    tot += sum(qi[a] * kj[a] for a in range(d))
+    tot += sum(qi[a] * qi[a] * kj[a] * kj[a] for a in range(d)) / 2
+    tot += sum(qi[a] * qi[b] * kj[a] * kj[b] for a in range(d) for b in range(a + 1, d))
+    return tot
+
+
 def _exact_outputs(fmap, q, k, v):
     n = len(q)
     out = []
     for i in range(n):
-        w = [_exact_kernel(fmap, q[i], k[j]) for j in range(i + 1)]
+        w = [_exact_kernel_sym(q[i], k[j]) if fmap == "taylor2sym"
+             else _exact_kernel(fmap, q[i], k[j]) for j in range(i + 1)]
         den = sum(w)
         out.append([sum(w[j] * v[j][c] for j in range(i + 1)) / den
                     for c in range(len(v[0]))])
@@ -109,9 +125,61 @@ def pin_exact_taylor2(o):
     _check_exact(o, "taylor2", nonneg=False)
 
 
+def pin_exact_taylor2_sym(o):
+    _check_exact(o, "taylor2sym", nonneg=False)
+
+
+def pin_taylor_sym_size_and_identity(o):
+    """SLA Knowl 7: the unordered-pair map has 1 + 3d/2 + d^2/2 features
+    (153 at d = 16); SLA Knowl 3: its kernel is still 1 + q.k + (q.k)^2/2."""
+    for d in (1, 2, 3, 16):
+        assert 2 * o.feature_dim("taylor2sym", d) == 2 + 3 * d + d * d
+    assert o.feature_dim("taylor2sym", 16) == 153
+    r = _rng(21)
+    q = r.standard_normal((40, 16)) * 0.6
+    k = r.standard_normal((40, 16)) * 0.6
+    s = np.sum(q * k, axis=-1)
+    got = o.kernel_value(q, k, "taylor2sym")
+    assert _rel(got, 1.0 + s + 0.5 * s * s) < 1e-13
+    assert o.feature_map(q, "taylor2sym").shape == (40, 153)
+
+
+def pin_taylor_sym_layout(o):
+    """Hand-written unordered-pair features of x = (1, 2, -3)."""
+    r2 = math.sqrt(2.0)
+    want = np.array([1.0, 1.0, 2.0, -3.0,
+                     1.0 / r2, 2.0, -3.0, 4.0 / r2, -6.0, 9.0 / r2])
+    got = o.feature_map(np.array([1.0, 2.0, -3.0]), "taylor2sym")
+    assert np.allclose(got, want, rtol=0, atol=1e-15)
+
+
+def pin_taylor_sym_fold(o):
+    """The unordered-pair state is the ordered-pair state folded: a square
+    row is kept, and the pair (a, b), a < b, is (S_ab + S_ba) / sqrt(2)."""
+    r = _rng(22)
+    d, dv = 4, 5
+    k = r.standard_normal((3, 30, d))
+    v = r.standard_normal((3, 30, dv))
+    S, z = o.final_state(k, v, "taylor2")
+    Ss, zs = o.final_state(k, v, "taylor2sym")
+    base = 1 + d
+    rows, zrows = [], []
+    for a in range(d):
+        for b in range(a, d):
+            ab, ba = base + a * d + b, base + b * d + a
+            if a == b:
+                rows.append(S[:, ab]); zrows.append(z[:, ab])
+            else:
+                rows.append((S[:, ab] + S[:, ba]) / math.sqrt(2.0))
+                zrows.append((z[:, ab] + z[:, ba]) / math.sqrt(2.0))
+    want_S = np.concatenate([S[:, :base], np.stack(rows, axis=1)], axis=1)
+    want_z = np.concatenate([z[:, :base], np.stack(zrows, axis=1)], axis=1)
+    assert _rel(Ss, want_S) < 1e-12 and _rel(zs, want_z) < 1e-12
+
+
 # ---------------------------------------------------------- equivalences ----
 def pin_quad_vs_rec(o):
-    for fmap in ("elu1", "taylor2"):
+    for fmap in ("elu1", "taylor2", "taylor2sym"):
         for seed, (b, n, dk, dv) in enumerate([(1, 1, 3, 2), (2, 2, 1, 1),
                                                (2, 17, 4, 3), (1, 64, 16, 8),
                                                (1, 256, 16, 16)]):
@@ -125,7 +193,7 @@ def pin_quad_vs_rec(o):
 
 
 def pin_rows_match_definition(o):
-    for fmap in ("elu1", "taylor2"):
+    for fmap in ("elu1", "taylor2", "taylor2sym"):
         r = _rng(7)
         q = r.standard_normal((40, 5))
         k = r.standard_normal((40, 5))
@@ -185,7 +253,7 @@ def pin_elu_torch(o):
 
 # ---------------------------------------------------- closed-form cases ----
 def pin_first_token(o):
-    for fmap in ("elu1", "taylor2"):
+    for fmap in ("elu1", "taylor2", "taylor2sym"):
         r = _rng(5)
         q = r.standard_normal((3, 1, 4))
         k = r.standard_normal((3, 1, 4))
@@ -201,7 +269,7 @@ def _cummean(v):
 
 
 def pin_constant_key(o):
-    for fmap in ("elu1", "taylor2"):
+    for fmap in ("elu1", "taylor2", "taylor2sym"):
         r = _rng(6)
         q = r.standard_normal((30, 4))
         k = np.tile(r.standard_normal((1, 4)), (30, 1))
@@ -222,7 +290,7 @@ def pin_zero_taylor_query(o):
 
 
 def pin_constant_and_linear_v(o):
-    for fmap in ("elu1", "taylor2"):
+    for fmap in ("elu1", "taylor2", "taylor2sym"):
         r = _rng(9)
         q = r.standard_normal((20, 3))
         k = r.standard_normal((20, 3))
@@ -238,7 +306,7 @@ def pin_constant_and_linear_v(o):
 
 
 def pin_convex_hull_and_positive(o):
-    for fmap in ("elu1", "taylor2"):
+    for fmap in ("elu1", "taylor2", "taylor2sym"):
         r = _rng(10)
         q = r.standard_normal((2, 300, 8))
         k = r.standard_normal((2, 300, 8))
@@ -259,7 +327,7 @@ def pin_convex_hull_and_positive(o):
 
 
 def pin_final_state(o):
-    for fmap, dk, dv in (("elu1", 6, 6), ("taylor2", 3, 13)):
+    for fmap, dk, dv in (("elu1", 6, 6), ("taylor2", 3, 13), ("taylor2sym", 3, 13)):
         r = _rng(11)
         q = r.standard_normal((2, 3, 33, dk))
         k = r.standard_normal((2, 3, 33, dk))
@@ -279,7 +347,7 @@ def pin_final_state(o):
 
 
 def pin_decode_continuation(o):
-    for fmap in ("elu1", "taylor2"):
+    for fmap in ("elu1", "taylor2", "taylor2sym"):
         r = _rng(12)
         q = r.standard_normal((2, 40, 4))
         k = r.standard_normal((2, 40, 4))
@@ -330,6 +398,10 @@ def pin_golden_handworked(o):
 PINS = [
     pin_exact_elu1,
     pin_exact_taylor2,
+    pin_exact_taylor2_sym,
+    pin_taylor_sym_size_and_identity,
+    pin_taylor_sym_layout,
+    pin_taylor_sym_fold,
     pin_quad_vs_rec,
     pin_rows_match_definition,
     pin_taylor_identity,

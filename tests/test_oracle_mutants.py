@@ -147,11 +147,50 @@ def _m_value_sign(o):
     o.decode_step = step
 
 
+def _sym_map(weight_sq, weight_off):
+    def phi(x):
+        x = np.asarray(x, dtype=np.float64)
+        d = x.shape[-1]
+        ones = np.ones(x.shape[:-1] + (1,))
+        pairs = [(a, b) for a in range(d) for b in range(a, d)]
+        quad = np.stack([x[..., a] * x[..., b] * (weight_sq if a == b else weight_off)
+                         for a, b in pairs], axis=-1)
+        return np.concatenate([ones, x, quad], axis=-1)
+    return phi
+
+
+def _m_sym_square_unscaled(o):
+    o.phi_taylor2_sym = _sym_map(1.0, 1.0)
+
+
+def _m_sym_pair_scaled(o):
+    o.phi_taylor2_sym = _sym_map(1.0 / math.sqrt(2.0), 1.0 / math.sqrt(2.0))
+
+
+def _m_sym_pair_doubled(o):
+    o.phi_taylor2_sym = _sym_map(1.0 / math.sqrt(2.0), math.sqrt(2.0))
+
+
+def _m_sym_lower_order(o):
+    # pairs listed column by column (lower triangle order): same values,
+    # different layout
+    def phi(x):
+        x = np.asarray(x, dtype=np.float64)
+        d = x.shape[-1]
+        ones = np.ones(x.shape[:-1] + (1,))
+        pairs = [(a, b) for b in range(d) for a in range(b + 1)]
+        quad = np.stack([x[..., a] * x[..., b] * (1.0 / math.sqrt(2.0) if a == b else 1.0)
+                         for a, b in pairs], axis=-1)
+        return np.concatenate([ones, x, quad], axis=-1)
+    o.phi_taylor2_sym = phi
+
+
 MUTANTS = [
     _m_elu_no_exp, _m_elu_plain_exp, _m_elu_missing_plus_one,
     _m_taylor_no_sqrt2, _m_taylor_no_constant, _m_taylor_wrong_layout,
     _m_mask_strict, _m_no_mask, _m_read_before_update, _m_den_uses_key,
     _m_state_transposed, _m_rows_off_by_one, _m_value_sign,
+    _m_sym_square_unscaled, _m_sym_pair_scaled, _m_sym_pair_doubled, _m_sym_lower_order,
 ]
 
 
