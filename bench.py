@@ -44,7 +44,11 @@ ROTATE_BYTES = 1 << 30         # rotate input sets over >= 1 GiB (> 256 MB MALL)
 
 
 def feature_dim(fmap, d_k):
-    return d_k if fmap == "elu1" else 1 + d_k + d_k * d_k
+    if fmap == "elu1":
+        return d_k
+    if fmap == "taylor2sym":
+        return 1 + d_k + d_k * (d_k + 1) // 2
+    return 1 + d_k + d_k * d_k
 
 
 def prefill_bytes(cfg):
@@ -123,19 +127,19 @@ def prefill_record(cfg, ms):
             "mfma_frac": prefill_flops(cfg) / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
-def time_decode(args, ops, synth, torch):
-    cfg = synth.WORKLOADS[DECODE]
+def time_decode(args, ops, synth, torch, fmap="taylor2"):
+    cfg = dict(synth.WORKLOADS[DECODE], fmap=fmap)
     dev = "cuda:0"
     pq, pk, pv, sq, sk, sv = synth.workload_inputs(DECODE, seed=0)
     qd, kd, vd = (ops.to_device(x, dev) for x in (pq, pk, pv))
-    _, (S, z) = ops.prefill(qd, kd, vd, "taylor2", return_state=True)
+    _, (S, z) = ops.prefill(qd, kd, vd, fmap, return_state=True)
     del qd, kd, vd
     T = cfg["steps"]
     steps = [ops.to_device(x, dev).permute(2, 0, 1, 3).contiguous() for x in (sq, sk, sv)]
     y = torch.empty((T, cfg["B"], cfg["H"], cfg["d_v"]), dtype=torch.bfloat16, device=dev)
     L = ops.load_library()
     stream = ops._stream(S)
-    calls = [(ops.MAPS["taylor2"], 1, cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"],
+    calls = [(ops.MAPS[fmap], 1, cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"],
               ops._ptr(steps[0][t]), ops._ptr(steps[1][t]), ops._ptr(steps[2][t]),
               ops._ptr(S), ops._ptr(z), ops._ptr(y[t]), stream) for t in range(T)]
 
@@ -428,6 +432,19 @@ def main():
                       "hbm_frac": dbytes / (dms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       "note": "the 128 steps captured in one HIP graph and replayed"},
         }
+        if not args.no_other_configs:
+            scfg, sms, sfinite, sms_graph = time_decode(args, ops, synth, torch,
+                                                        "taylor2sym")
+            sbytes = decode_step_bytes(scfg)
+            out["decode"]["unordered_pairs"] = {
+                "workload": (f"the same decode with the unordered-pair Taylor map "
+                             f"(D={feature_dim('taylor2sym', scfg['d_k'])})"),
+                "ms_per_step": sms, "steps_per_s": 1e3 / sms, "finite": sfinite,
+                "algorithmic_bytes": sbytes,
+                "hbm_frac": sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "graph_ms_per_step": sms_graph,
+                "graph_hbm_frac": sbytes / (sms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth)
         if not args.no_decode:

@@ -26,7 +26,10 @@ constexpr int64_t kMinSegChunks = 8;    // shortest default segment (chunks)
 constexpr int64_t kMaxSegBytes = ((int64_t)1 << 31) - 4096;
 constexpr int64_t kMaxElems = (int64_t)1 << 46;
 
-#define LINATTN_FOR_SHAPES(X)                                                 \
+// Shapes built as prefill kernels.  The unordered-pair Taylor map runs on
+// the ordered-pair prefill kernels (PrefillArgs::sym), so it is listed only
+// among the decode shapes.
+#define LINATTN_FOR_PREFILL_SHAPES(X)                                         \
   X(MAP_ELU1, 16, 16)                                                         \
   X(MAP_ELU1, 32, 32)                                                         \
   X(MAP_ELU1, 64, 64)                                                         \
@@ -34,8 +37,25 @@ constexpr int64_t kMaxElems = (int64_t)1 << 46;
   X(MAP_TAYLOR2, 16, 32)                                                      \
   X(MAP_TAYLOR2, 16, 64)
 
+#define LINATTN_FOR_SHAPES(X)                                                 \
+  LINATTN_FOR_PREFILL_SHAPES(X)                                               \
+  X(MAP_TAYLOR2_SYM, 16, 16)                                                  \
+  X(MAP_TAYLOR2_SYM, 16, 32)                                                  \
+  X(MAP_TAYLOR2_SYM, 16, 64)
+
+static_assert((int)LINATTN_MAP_ELU1 == MAP_ELU1 &&
+                  (int)LINATTN_MAP_TAYLOR2 == MAP_TAYLOR2 &&
+                  (int)LINATTN_MAP_TAYLOR2_SYM == MAP_TAYLOR2_SYM,
+              "map codes of the ABI and the kernels agree");
+
 bool valid_map(int map) {
-  return map == LINATTN_MAP_ELU1 || map == LINATTN_MAP_TAYLOR2;
+  return map == LINATTN_MAP_ELU1 || map == LINATTN_MAP_TAYLOR2 ||
+         map == LINATTN_MAP_TAYLOR2_SYM;
+}
+
+// The map whose prefill kernels run `map`.
+int prefill_map(int map) {
+  return map == LINATTN_MAP_TAYLOR2_SYM ? MAP_TAYLOR2 : map;
 }
 
 bool valid_dtype(int dtype) {
@@ -55,13 +75,15 @@ int64_t feature_dim(int map, int64_t dk) {
   if (dk <= 0 || dk > (1 << 20)) return -1;
   if (map == LINATTN_MAP_ELU1) return dk;
   if (map == LINATTN_MAP_TAYLOR2) return 1 + dk + dk * dk;
+  if (map == LINATTN_MAP_TAYLOR2_SYM) return 1 + dk + dk * (dk + 1) / 2;
   return -1;
 }
 
 int64_t slot_floats(int map, int64_t dk, int64_t dv) {
+  map = prefill_map(map);
 #define X(M, DK, DV) \
   if (map == M && dk == DK && dv == DV) return StateShape<M, DK, DV>::SLOT;
-  LINATTN_FOR_SHAPES(X)
+  LINATTN_FOR_PREFILL_SHAPES(X)
 #undef X
   return -1;
 }
@@ -121,11 +143,12 @@ size_t workspace_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nseg) {
 
 hipError_t dispatch_prefill(int map, int dtype, int64_t dk, int64_t dv,
                             const PrefillArgs& a, hipStream_t st) {
+  map = prefill_map(map);
 #define X(M, DK, DV)                                                     \
   if (map == M && dk == DK && dv == DV)                                  \
     return dtype == LINATTN_DTYPE_F32 ? launch_prefill<M, float, DK, DV>(a, st) \
                                       : launch_prefill<M, bf16_t, DK, DV>(a, st);
-  LINATTN_FOR_SHAPES(X)
+  LINATTN_FOR_PREFILL_SHAPES(X)
 #undef X
   return hipErrorInvalidValue;
 }
@@ -194,10 +217,14 @@ linattn_status_t linattn_feature_map(int map, int dtype, const void* x,
     e = dtype == LINATTN_DTYPE_F32
             ? launch_feature_map<MAP_ELU1, float>(x, rows, (int)d_k, phi, st)
             : launch_feature_map<MAP_ELU1, bf16_t>(x, rows, (int)d_k, phi, st);
-  else
+  else if (map == LINATTN_MAP_TAYLOR2)
     e = dtype == LINATTN_DTYPE_F32
             ? launch_feature_map<MAP_TAYLOR2, float>(x, rows, (int)d_k, phi, st)
             : launch_feature_map<MAP_TAYLOR2, bf16_t>(x, rows, (int)d_k, phi, st);
+  else
+    e = dtype == LINATTN_DTYPE_F32
+            ? launch_feature_map<MAP_TAYLOR2_SYM, float>(x, rows, (int)d_k, phi, st)
+            : launch_feature_map<MAP_TAYLOR2_SYM, bf16_t>(x, rows, (int)d_k, phi, st);
   return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
@@ -290,6 +317,7 @@ linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,
   a.nseg = nseg;
   a.seg_chunks = seg_chunks;
   a.prefix_mode = nseg == 1 ? 0 : (nseg <= kDirectPrefixMax ? 1 : 2);
+  a.sym = map == LINATTN_MAP_TAYLOR2_SYM ? 1 : 0;
   const hipError_t e =
       dispatch_prefill(map, dtype, d_k, d_v, a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;

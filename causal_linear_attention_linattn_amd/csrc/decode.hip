@@ -19,8 +19,24 @@
 
 namespace linattn {
 
+// Quadratic feature p (0-based, after the constant and linear ones) of the
+// unordered-pair map: pairs a <= b in row-major upper-triangular order,
+// weight 1/sqrt 2 on the squares and 1 on the cross products.
+template <typename F>
+__device__ __forceinline__ float sym_pair_feature(int p, int d, F&& xat) {
+  int a = 0;
+  while (p >= d - a) {
+    p -= d - a;
+    ++a;
+  }
+  const int b = a + p;
+  const float xa = xat(a);
+  return a == b ? xa * xa * kInvSqrt2 : xa * xat(b);
+}
+
 // Feature r of phi(x) in the exported order: ELU1 elementwise; TAYLOR2
-// [1, x, vec(x x^T)/sqrt 2] with pair (a, b) at 1 + d + a d + b.
+// [1, x, vec(x x^T)/sqrt 2] with pair (a, b) at 1 + d + a d + b;
+// TAYLOR2_SYM [1, x, unordered pairs].
 template <int MAP, int DK>
 __device__ __forceinline__ float feature_ext(const float* x, int r) {
   if constexpr (MAP == MAP_ELU1) {
@@ -29,6 +45,8 @@ __device__ __forceinline__ float feature_ext(const float* x, int r) {
     if (r == 0) return 1.0f;
     if (r <= DK) return x[r - 1];
     const int rr = r - 1 - DK;
+    if constexpr (MAP == MAP_TAYLOR2_SYM)
+      return sym_pair_feature(rr, DK, [&](int i) { return x[i]; });
     return x[rr / DK] * x[rr % DK] * kInvSqrt2;
   }
 }
@@ -189,6 +207,9 @@ __global__ __launch_bounds__(256) void feature_map_kernel(const T* __restrict__ 
         val = 1.0f;
       } else if (r <= dk) {
         val = E::to_f32(xr[r - 1]);
+      } else if constexpr (MAP == MAP_TAYLOR2_SYM) {
+        val = sym_pair_feature(r - 1 - dk, dk,
+                               [&](int i) { return E::to_f32(xr[i]); });
       } else {
         const int rr = r - 1 - dk;
         val = E::to_f32(xr[rr / dk]) * E::to_f32(xr[rr % dk]) * kInvSqrt2;
@@ -201,7 +222,9 @@ __global__ __launch_bounds__(256) void feature_map_kernel(const T* __restrict__ 
 template <int MAP, typename T>
 hipError_t launch_feature_map(const void* x, int64_t rows, int d_k, float* phi,
                               hipStream_t st) {
-  const int64_t D = MAP == MAP_ELU1 ? d_k : 1 + d_k + (int64_t)d_k * d_k;
+  const int64_t D = MAP == MAP_ELU1      ? d_k
+                    : MAP == MAP_TAYLOR2 ? 1 + d_k + (int64_t)d_k * d_k
+                                         : 1 + d_k + (int64_t)d_k * (d_k + 1) / 2;
   const int64_t total = rows * D;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 16384) blocks = 16384;
@@ -226,10 +249,15 @@ LINATTN_DECODE_INST(MAP_ELU1, 64, 64)
 LINATTN_DECODE_INST(MAP_TAYLOR2, 16, 16)
 LINATTN_DECODE_INST(MAP_TAYLOR2, 16, 32)
 LINATTN_DECODE_INST(MAP_TAYLOR2, 16, 64)
+LINATTN_DECODE_INST(MAP_TAYLOR2_SYM, 16, 16)
+LINATTN_DECODE_INST(MAP_TAYLOR2_SYM, 16, 32)
+LINATTN_DECODE_INST(MAP_TAYLOR2_SYM, 16, 64)
 
 template hipError_t launch_feature_map<MAP_ELU1, float>(const void*, int64_t, int, float*, hipStream_t);
 template hipError_t launch_feature_map<MAP_ELU1, bf16_t>(const void*, int64_t, int, float*, hipStream_t);
 template hipError_t launch_feature_map<MAP_TAYLOR2, float>(const void*, int64_t, int, float*, hipStream_t);
 template hipError_t launch_feature_map<MAP_TAYLOR2, bf16_t>(const void*, int64_t, int, float*, hipStream_t);
+template hipError_t launch_feature_map<MAP_TAYLOR2_SYM, float>(const void*, int64_t, int, float*, hipStream_t);
+template hipError_t launch_feature_map<MAP_TAYLOR2_SYM, bf16_t>(const void*, int64_t, int, float*, hipStream_t);
 
 }  // namespace linattn

@@ -75,38 +75,62 @@ template <bool OUT>
 constexpr int kRing = OUT ? 2 : 4;
 
 // Internal feature row -> exported row (or -1 for padding) and the factor
-// that converts an exported value into the internal one.
+// that converts an exported value into the internal one.  Internal rows
+// 0..255 hold the ordered pairs (a, b) = (r / 16, r % 16) with key feature
+// k_a k_b, row 256 the constant and 257..272 the linear features.
+//   ordered export: pair (a, b) at 17 + 16 a + b, value internal / sqrt 2;
+//   unordered export (sym): pair {a, b} at 17 + p(min, max) with
+//     p(a, b) = a d - a (a - 1) / 2 + (b - a), value internal for a != b and
+//     internal / sqrt 2 for a == b.  Both (a, b) and (b, a) import from the
+//     same exported row; only a <= b is exported (`owner`).
 template <int MAP, int DK>
-__device__ __forceinline__ int ext_row(int r, float& to_internal) {
+__device__ __forceinline__ int ext_row(int r, bool sym, float& to_internal,
+                                       bool& owner) {
   to_internal = 1.0f;
+  owner = true;
   if (MAP == MAP_ELU1) return r < DK ? r : -1;
   if (r < 256) {
-    to_internal = kSqrt2;
-    return 17 + r;
+    if (!sym) {
+      to_internal = kSqrt2;
+      return 17 + r;
+    }
+    const int pa = r >> 4, pb = r & 15;
+    const int lo = pa < pb ? pa : pb, hi = pa < pb ? pb : pa;
+    owner = pa <= pb;
+    if (pa == pb) to_internal = kSqrt2;
+    return 17 + lo * DK - lo * (lo - 1) / 2 + (hi - lo);
   }
   return r < 273 ? r - 256 : -1;
+}
+
+// Exported feature rows of a head's state.
+template <int MAP, int DK, int DV>
+__device__ __forceinline__ int ext_rows(bool sym) {
+  return MAP == MAP_TAYLOR2 && sym ? kSymD<DK> : StateShape<MAP, DK, DV>::D;
 }
 
 // One lane's 4 values of state tile (rt, ct) read from the exported
 // layout S [D, DV], z [D] of sequence bh, converted to the internal one.
 template <int MAP, int DK, int DV>
 __device__ __forceinline__ f32x4_t state_in_tile(const float* S_in,
-                                                 const float* z_in, int bh,
-                                                 int rt, int ct, int lane) {
-  using SS = StateShape<MAP, DK, DV>;
+                                                 const float* z_in, bool sym,
+                                                 int bh, int rt, int ct,
+                                                 int lane) {
+  const int D = ext_rows<MAP, DK, DV>(sym);
   f32x4_t r;
   const int col = 16 * ct + (lane & 15);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int row = 16 * rt + 4 * (lane >> 4) + t;
     float f;
-    const int e = ext_row<MAP, DK>(row, f);
+    bool owner;
+    const int e = ext_row<MAP, DK>(row, sym, f, owner);
     float val = 0.0f;
     if (e >= 0) {
       if (col < DV)
-        val = S_in[((size_t)bh * SS::D + e) * DV + col];
+        val = S_in[((size_t)bh * D + e) * DV + col];
       else if (col == DV)
-        val = z_in[(size_t)bh * SS::D + e];
+        val = z_in[(size_t)bh * D + e];
     }
     r[t] = val * f;
   }
@@ -115,22 +139,24 @@ __device__ __forceinline__ f32x4_t state_in_tile(const float* S_in,
 
 template <int MAP, int DK, int DV>
 __device__ __forceinline__ void state_out_tile(float* S_out, float* z_out,
-                                               int bh, int rt, int ct,
-                                               int lane, const f32x4_t& v) {
-  using SS = StateShape<MAP, DK, DV>;
+                                               bool sym, int bh, int rt,
+                                               int ct, int lane,
+                                               const f32x4_t& v) {
+  const int D = ext_rows<MAP, DK, DV>(sym);
   const int col = 16 * ct + (lane & 15);
   if (col > DV) return;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int row = 16 * rt + 4 * (lane >> 4) + t;
     float f;
-    const int e = ext_row<MAP, DK>(row, f);
-    if (e < 0) continue;
+    bool owner;
+    const int e = ext_row<MAP, DK>(row, sym, f, owner);
+    if (e < 0 || !owner) continue;
     const float val = v[t] / f;
     if (col < DV)
-      S_out[((size_t)bh * SS::D + e) * DV + col] = val;
+      S_out[((size_t)bh * D + e) * DV + col] = val;
     else
-      z_out[(size_t)bh * SS::D + e] = val;
+      z_out[(size_t)bh * D + e] = val;
   }
 }
 
@@ -360,7 +386,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
               a.ws + ((size_t)bh * a.nseg + seg) * SH::SLOT);
           s = p[(rt * NCT + ct) * 64 + lane];
         } else if (a.S_in != nullptr) {
-          s = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, bh, rt, ct, lane);
+          s = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, a.sym != 0, bh, rt, ct,
+                                        lane);
         }
       }
       Sacc[m][ct] = s;
@@ -822,8 +849,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
         if (rt >= NRT) continue;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
-          state_out_tile<MAP, DK, DV>(a.S_out, a.z_out, bh, rt, ct, lane,
-                                      Sacc[m][ct]);
+          state_out_tile<MAP, DK, DV>(a.S_out, a.z_out, a.sym != 0, bh, rt,
+                                      ct, lane, Sacc[m][ct]);
       }
     }
   } else {
@@ -855,7 +882,8 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(PrefillArgs a) {
   if (a.S_in != nullptr) {
     const int rt = e4 / (SS::NCT * 64);
     const int ct = (e4 / 64) % SS::NCT;
-    run = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, bh, rt, ct, e4 % 64);
+    run = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, a.sym != 0, bh, rt, ct,
+                                    e4 % 64);
   }
   f32x4_t* p = reinterpret_cast<f32x4_t*>(a.ws + (size_t)bh * a.nseg * SS::SLOT) + e4;
   p[0] = run;

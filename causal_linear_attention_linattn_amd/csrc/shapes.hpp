@@ -7,7 +7,15 @@
 
 namespace linattn {
 
-enum { MAP_ELU1 = 0, MAP_TAYLOR2 = 1 };
+// MAP_TAYLOR2_SYM has the same kernel as MAP_TAYLOR2 but counts each
+// unordered pair of key coordinates once.  The prefill runs it on the
+// MAP_TAYLOR2 kernels, which differ only in how a state is imported and
+// exported (PrefillArgs::sym).
+enum { MAP_ELU1 = 0, MAP_TAYLOR2 = 1, MAP_TAYLOR2_SYM = 2 };
+
+// Exported feature rows of the unordered-pair map: 1 + d + d (d + 1) / 2.
+template <int DK>
+constexpr int kSymD = 1 + DK + DK * (DK + 1) / 2;
 
 // Most segments per head for which each output workgroup adds up the sums
 // of its preceding segments itself (prefix_mode 1); beyond it a scan kernel
@@ -30,11 +38,15 @@ struct PrefillArgs {
   int seg_chunks;  // chunks per segment
   int prefix_mode; // 0: one segment; 1: output workgroups add the preceding
                    // segment sums themselves; 2: a scan kernel runs first
+  int sym;         // MAP_TAYLOR2 only: S_in/S_out use the unordered-pair
+                   // layout (kSymD rows) instead of the ordered one
 };
 
 template <int MAP, int DK, int DV>
 struct StateShape {
-  static constexpr int D = MAP == MAP_ELU1 ? DK : 1 + DK + DK * DK;
+  static constexpr int D = MAP == MAP_ELU1      ? DK
+                           : MAP == MAP_TAYLOR2 ? 1 + DK + DK * DK
+                                                : kSymD<DK>;
   static constexpr int DP = MAP == MAP_ELU1 ? ((DK + 31) / 32) * 32 : 288;
   static constexpr int NRT = DP / 16;    // 16-row tiles of S'
   static constexpr int NKB = DP / 32;    // 32-wide K blocks over features

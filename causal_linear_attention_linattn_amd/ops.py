@@ -21,7 +21,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "liblinattn.so")
 
-MAPS = {"elu1": 0, "taylor2": 1}
+MAPS = {"elu1": 0, "taylor2": 1, "taylor2sym": 2}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace",
            4: "hip error"}

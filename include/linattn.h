@@ -18,6 +18,17 @@
  *                       (feature 1 + d_k + a*d_k + b is x_a x_b / sqrt 2);
  *                       D = 1 + d_k + d_k^2, so phi(q).phi(k) = 1 + q.k +
  *                       (q.k)^2/2 (same page, Knowl 3).
+ *   LINATTN_MAP_TAYLOR2_SYM  the same kernel with each unordered pair of
+ *                       coordinates counted once: phi(x) = [1, x, w_ab x_a x_b
+ *                       for a <= b], pairs in row-major upper-triangular
+ *                       order (feature 1 + d_k + a*d_k - a(a-1)/2 + (b-a)),
+ *                       w_aa = 1/sqrt(2), w_ab = 1 for a < b;
+ *                       D = 1 + d_k + d_k(d_k+1)/2 = 153 at d_k = 16, the
+ *                       state size of the generation-state accounting (same
+ *                       page, Knowl 7).  phi(q).phi(k) equals TAYLOR2's.
+ *                       Its state relates to TAYLOR2's by
+ *                       S_sym[{a,b}] = (S[a,b] + S[b,a]) / sqrt(2), a < b, and
+ *                       S_sym[{a,a}] = S[a,a].
  *
  * Conventions shared by every call:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
@@ -36,6 +47,7 @@
  *   - Supported shapes (anything else returns LINATTN_ERR_UNSUPPORTED):
  *       ELU1:    d_k == d_v in {16, 32, 64}
  *       TAYLOR2: d_k == 16, d_v in {16, 32, 64}   (D = 273)
+ *       TAYLOR2_SYM: d_k == 16, d_v in {16, 32, 64}   (D = 153)
  *     for both dtypes, any B, H >= 1 and any N >= 1 (ragged tails are
  *     masked inside the kernels).
  */
@@ -59,7 +71,8 @@ typedef enum linattn_status {
 
 typedef enum linattn_map {
   LINATTN_MAP_ELU1 = 0,
-  LINATTN_MAP_TAYLOR2 = 1
+  LINATTN_MAP_TAYLOR2 = 1,
+  LINATTN_MAP_TAYLOR2_SYM = 2
 } linattn_map_t;
 
 typedef enum linattn_dtype {
@@ -73,7 +86,8 @@ const char* linattn_status_string(int status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int linattn_version(void);
 
-/* Feature dimension D of a map: ELU1 -> d_k; TAYLOR2 -> 1 + d_k + d_k^2.
+/* Feature dimension D of a map: ELU1 -> d_k; TAYLOR2 -> 1 + d_k + d_k^2;
+   TAYLOR2_SYM -> 1 + d_k + d_k(d_k+1)/2.
    Returns -1 for an unknown map or d_k <= 0. */
 int64_t linattn_feature_dim(int map, int64_t d_k);
 
@@ -145,7 +159,7 @@ linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,
  * All arithmetic is float32 (inputs are widened); y is rounded to dtype.
  * y must not overlap S or z.  A zero state is valid input only if the step's
  * own token makes the denominator positive (it always does: phi(k) > 0 for
- * ELU1 and phi(q).phi(k) >= 1/2 for TAYLOR2).
+ * ELU1 and phi(q).phi(k) >= 1/2 for both Taylor maps).
  */
 linattn_status_t linattn_decode_step(int map, int dtype, int64_t B, int64_t H,
                                      int64_t d_k, int64_t d_v, const void* q,

@@ -68,15 +68,19 @@ def test_feature_dim_and_supported(lib):
     assert lib.linattn_feature_dim(0, 64) == 64
     assert lib.linattn_feature_dim(1, 16) == 273
     assert lib.linattn_feature_dim(1, 3) == 13
+    assert lib.linattn_feature_dim(2, 16) == 153
+    assert lib.linattn_feature_dim(2, 3) == 10
     assert lib.linattn_feature_dim(7, 16) == -1
     assert lib.linattn_feature_dim(0, 0) == -1
     for dt in (0, 1):
         for d in (16, 32, 64):
             assert lib.linattn_supported(0, dt, d, d) == 1
             assert lib.linattn_supported(1, dt, 16, d) == 1
+            assert lib.linattn_supported(2, dt, 16, d) == 1
         assert lib.linattn_supported(0, dt, 64, 32) == 0
         assert lib.linattn_supported(0, dt, 128, 128) == 0
         assert lib.linattn_supported(1, dt, 32, 64) == 0
+        assert lib.linattn_supported(2, dt, 32, 32) == 0
     assert lib.linattn_supported(0, 2, 64, 64) == 0
     for s in range(6):
         assert lib.linattn_status_string(s)
@@ -94,6 +98,8 @@ def test_workspace_bytes(lib):
     assert f(0, 1, 8, 8, 4096, 64, 64, 4096) == 0
     slot_tay = 18 * 5 * 256
     assert f(1, 1, 8, 16, 2048, 16, 64, 512) == 128 * 4 * slot_tay * 4
+    # the unordered-pair map runs on the same kernels and workspace
+    assert f(2, 1, 8, 16, 2048, 16, 64, 512) == 128 * 4 * slot_tay * 4
     # ragged: 65 tokens in 64-token segments -> 2 segments
     assert f(0, 0, 1, 1, 65, 16, 16, 64) == 2 * (2 * 2 * 256) * 4
     assert f(0, 1, 1, 1, 4096, 64, 64, 100) == bad     # not a multiple of 64

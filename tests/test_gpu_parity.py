@@ -62,7 +62,7 @@ def gpu_prefill(q, k, v, fmap, **kw):
 
 # ------------------------------------------------------------ feature map --
 @pytest.mark.parametrize("fmap,d_k", [("elu1", 16), ("elu1", 32), ("elu1", 64),
-                                      ("taylor2", 16)])
+                                      ("taylor2", 16), ("taylor2sym", 16)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_feature_map(fmap, d_k, dtype):
     _log(f"feature_map {fmap} d_k={d_k} {dtype}")
@@ -102,7 +102,13 @@ def test_tiny_fp32_prefill_and_decode_match_definition():
 
 # ----------------------------------------------- small shapes, every kernel --
 SHAPES = [("elu1", 16, 16), ("elu1", 32, 32), ("elu1", 64, 64),
-          ("taylor2", 16, 16), ("taylor2", 16, 32), ("taylor2", 16, 64)]
+          ("taylor2", 16, 16), ("taylor2", 16, 32), ("taylor2", 16, 64),
+          ("taylor2sym", 16, 16), ("taylor2sym", 16, 32), ("taylor2sym", 16, 64)]
+
+
+def _qk_scale(fmap):
+    """Taylor maps take q, k scaled by d'^(-1/4), as a model applies them."""
+    return 16.0 ** -0.25 if fmap.startswith("taylor2") else 1.0
 
 
 @pytest.mark.parametrize("fmap,d_k,d_v", SHAPES)
@@ -111,7 +117,7 @@ SHAPES = [("elu1", 16, 16), ("elu1", 32, 32), ("elu1", 64, 64),
                                        (517, 128), (700, 0)])
 def test_prefill_small(fmap, d_k, d_v, dtype, N, seg_len):
     _log(f"prefill {fmap} {d_k}x{d_v} {dtype} N={N} seg_len={seg_len}")
-    scale = 16.0 ** -0.25 if fmap == "taylor2" else 1.0
+    scale = _qk_scale(fmap)
     q, k, v = synth.draw_qkv(2, 3, N, d_k, d_v, seed=N, dtype=dtype, qk_scale=scale)
     y_ref, S_ref, z_ref = oracle.attention_recurrent(q.f64(), k.f64(), v.f64(), fmap)
     y, (S, z) = gpu_prefill(q, k, v, fmap, return_state=True, seg_len=seg_len)
@@ -121,13 +127,14 @@ def test_prefill_small(fmap, d_k, d_v, dtype, N, seg_len):
     assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
 
 
-@pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64)])
+@pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64),
+                                         ("taylor2sym", 16, 64)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prefill_continues_from_state(fmap, d_k, d_v, dtype):
     """prefill(N1) -> state -> prefill(N2, state) == oracle over N1 + N2;
     also in place (S_out is S_in)."""
     _log(f"prefill continuation {fmap} {dtype}")
-    scale = 16.0 ** -0.25 if fmap == "taylor2" else 1.0
+    scale = _qk_scale(fmap)
     q, k, v = synth.draw_qkv(1, 4, 448, d_k, d_v, seed=5, dtype=dtype, qk_scale=scale)
     y_ref, S_ref, z_ref = oracle.attention_recurrent(q.f64(), k.f64(), v.f64(), fmap)
     qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
@@ -162,7 +169,7 @@ def test_prefill_continues_from_state(fmap, d_k, d_v, dtype):
 @pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64)])
 def test_prefill_deterministic_and_segment_invariant(fmap, d_k, d_v):
     _log(f"determinism / segment invariance {fmap}")
-    scale = 16.0 ** -0.25 if fmap == "taylor2" else 1.0
+    scale = _qk_scale(fmap)
     q, k, v = synth.draw_qkv(2, 2, 1000, d_k, d_v, seed=3, dtype="bf16", qk_scale=scale)
     y_ref = oracle.attention_recurrent(q.f64(), k.f64(), v.f64(), fmap)[0]
     outs = {}
@@ -174,6 +181,35 @@ def test_prefill_deterministic_and_segment_invariant(fmap, d_k, d_v):
         outs[seg_len] = a
     for s, a in outs.items():
         assert row_err(a, outs[1024]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("seg_len", [0, 64])
+def test_unordered_pair_state_is_the_folded_ordered_state(seg_len):
+    """Same inputs through both Taylor maps: the unordered-pair final state
+    equals the ordered one folded, (S[a,b] + S[b,a]) / sqrt 2 off the
+    diagonal and S[a,a] on it; the outputs agree, since the kernels do."""
+    _log(f"taylor2sym vs folded taylor2 state, seg_len={seg_len}")
+    q, k, v = synth.draw_qkv(2, 3, 300, 16, 32, seed=8, dtype="f32",
+                             qk_scale=_qk_scale("taylor2"))
+    y_o, (S_o, z_o) = gpu_prefill(q, k, v, "taylor2", return_state=True, seg_len=seg_len)
+    y_s, (S_s, z_s) = gpu_prefill(q, k, v, "taylor2sym", return_state=True, seg_len=seg_len)
+    S_o, z_o = ops.to_numpy64(S_o), ops.to_numpy64(z_o)
+    S_s, z_s = ops.to_numpy64(S_s), ops.to_numpy64(z_s)
+    d = 16
+    sq = S_o[:, :, 1 + d:].reshape(2, 3, d, d, 32)
+    zq = z_o[:, :, 1 + d:].reshape(2, 3, d, d)
+    fold_S = [S_o[:, :, :1 + d]]
+    fold_z = [z_o[:, :, :1 + d]]
+    for a, b in oracle.sym_pairs(d):
+        if a == b:
+            fold_S.append(sq[:, :, a, a][:, :, None])
+            fold_z.append(zq[:, :, a, a][:, :, None])
+        else:
+            fold_S.append(((sq[:, :, a, b] + sq[:, :, b, a]) / np.sqrt(2))[:, :, None])
+            fold_z.append(((zq[:, :, a, b] + zq[:, :, b, a]) / np.sqrt(2))[:, :, None])
+    assert state_err(S_s, np.concatenate(fold_S, axis=2)) <= 1e-5
+    assert state_err(z_s[..., None], np.concatenate(fold_z, axis=2)[..., None]) <= 1e-5
+    assert row_err(ops.to_numpy64(y_s), ops.to_numpy64(y_o)) <= 1e-5
 
 
 # ----------------------------------------------------------------- decode --
@@ -282,17 +318,18 @@ def test_full_size_prefill(name, heads):
         assert state_err(S[b, h][None, None], S_ref[None, None]) <= TOL["bf16"]
 
 
-def test_full_size_decode_after_prefill():
+@pytest.mark.parametrize("fmap", ["taylor2", "taylor2sym"])
+def test_full_size_decode_after_prefill(fmap):
     """256 sequences x 16 heads, Taylor d'=16: the state seeded by the
     library's own prefill over a 1024-token prefix, then 128 decode steps.
     Sampled heads are checked against the oracle's recurrence over all
     1024 + 128 tokens; every output row must lie in the convex hull."""
-    _log("full-size decode (prefill 1024 + 128 steps)")
+    _log(f"full-size decode {fmap} (prefill 1024 + 128 steps)")
     name = "decode_taylor2_bf16"
     cfg = synth.WORKLOADS[name]
     pq, pk, pv, sq, sk, sv = synth.workload_inputs(name, seed=0)
     qd, kd, vd = (ops.to_device(x, DEV) for x in (pq, pk, pv))
-    _, (Sd, zd) = ops.prefill(qd, kd, vd, "taylor2", return_state=True)
+    _, (Sd, zd) = ops.prefill(qd, kd, vd, fmap, return_state=True)
     del qd, kd, vd
     sqd, skd, svd = (ops.to_device(x, DEV) for x in (sq, sk, sv))
     T = cfg["steps"]
@@ -302,7 +339,7 @@ def test_full_size_decode_after_prefill():
     step_k = skd.permute(2, 0, 1, 3).contiguous()
     step_v = svd.permute(2, 0, 1, 3).contiguous()
     for t in range(T):
-        ops.decode_step(step_q[t], step_k[t], step_v[t], Sd, zd, "taylor2", out=ys[t])
+        ops.decode_step(step_q[t], step_k[t], step_v[t], Sd, zd, fmap, out=ys[t])
     torch.cuda.synchronize()
     y = ops.to_numpy64(ys)                       # [T, B, H, d_v]
     assert np.all(np.isfinite(y))
@@ -324,9 +361,9 @@ def test_full_size_decode_after_prefill():
         ka = np.concatenate([_f32(pk, b, h), _f32(sk, b, h)]).astype(np.float64)
         va = np.concatenate([_f32(pv, b, h), _f32(sv, b, h)]).astype(np.float64)
         rows = list(range(cfg["N"], cfg["N"] + T))
-        ref = oracle.attention_rows(qa, ka, va, "taylor2", rows)
+        ref = oracle.attention_rows(qa, ka, va, fmap, rows)
         assert row_err(y[:, b, h], ref) <= TOL["bf16"], (b, h)
-        S_ref, _ = oracle.final_state(ka, va, "taylor2")
+        S_ref, _ = oracle.final_state(ka, va, fmap)
         assert state_err(S[b, h][None, None], S_ref[None, None]) <= TOL["bf16"]
 
 
