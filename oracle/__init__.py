@@ -8,13 +8,19 @@ from .linattn_oracle import (  # noqa: F401
     MAPS,
     TAYLOR2,
     TAYLOR2_SYM,
+    attention_gated_quadratic,
+    attention_gated_recurrent,
+    attention_gated_rows,
     attention_quadratic,
     attention_recurrent,
     attention_rows,
+    decay_matrix,
     decode_step,
     feature_dim,
     feature_map,
     final_state,
+    gated_decode_step,
+    gated_final_state,
     kernel_value,
     phi_elu1,
     phi_taylor2,

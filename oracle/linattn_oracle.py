@@ -14,6 +14,12 @@ Sources (page titles as printed; section in brackets):
         the recurrent state equations, the Taylor kernel identity) and Knowl 5
         (prefill writes final states; generation updates the state, then reads
         it).
+  [HN]  the discussion page of "Transformers are RNNs" (hackerpapers),
+        section "In the conversation": one comment writes the gated linear
+        recurrences as a state decayed by a forget factor plus a gated outer
+        product k v^T, read as C^T q; another describes the state-space layer
+        whose transition is a scalar times the identity as causal linear
+        attention with the coefficients a_1 ... a_t compounded.
 
 Everything here is plain float64 numpy.  The functions follow the
 definitions as written; there is no chunking, blocking or fusion.
@@ -33,6 +39,15 @@ Readings taken where the pages are silent (each is listed in the design doc):
   * No epsilon in the denominator; it is positive for both maps.
   * Generation updates the state first and then reads it ([SLA] Knowl 3
     recurrent equations; Knowl 5 second paragraph).
+  * Scalar decay ([HN]): one coefficient a_t per sequence, head and position
+    multiplies the whole state (S and z) before token t is added:
+    S_t = a_t S_{t-1} + phi(k_t)^T v_t, z_t = a_t z_{t-1} + phi(k_t)^T.  The
+    forget factor of the comment is a_t times the identity; its input gate is
+    left to the caller (it can be folded into k_t or v_t).  Unrolled, token j
+    enters the state at position i >= j with weight a_{j+1} ... a_i (1 for
+    j = i).  The output is either the [SLA] Knowl 3 ratio of the decayed sums
+    (normalize=True) or the comment's unnormalised read phi(q_t) S_t
+    (normalize=False).
 
 Parity pins (all in tests/test_oracle_pins.py): exact rational brute force,
 quadratic == recurrent, Taylor identity and its exp limit, torch's elu,
@@ -224,6 +239,137 @@ def final_state(k, v, fmap: str):
     S = np.swapaxes(fk, -1, -2) @ v
     z = fk.sum(axis=-2)
     return S, z
+
+
+# --------------------------------------------------------------------------
+# Scalar-decay (gated) form
+# --------------------------------------------------------------------------
+def decay_matrix(a) -> np.ndarray:
+    """W[..., i, j] = a_{j+1} a_{j+2} ... a_i for j <= i (an empty product, 1,
+    on the diagonal) and 0 for j > i: the compounded coefficients of the
+    scalar-transition state-space form ([HN] comment on the duality).
+
+    a: [..., N].  Built column by column from explicit products (no
+    logarithms), so a_t = 0 gives exact zeros.  O(N^2): small N only.
+    """
+    a = _f64(a)
+    n = a.shape[-1]
+    W = np.zeros(a.shape[:-1] + (n, n), dtype=np.float64)
+    for i in range(n):
+        W[..., i, i] = 1.0
+        for j in range(i - 1, -1, -1):
+            W[..., i, j] = W[..., i, j + 1] * a[..., j + 1]
+    return W
+
+
+def attention_gated_quadratic(q, k, v, a, fmap: str, normalize=True) -> np.ndarray:
+    """Gated causal output, definition form.
+
+    y_i = sum_{j<=i} W_ij phi(q_i).phi(k_j) v_j  [/ sum_{j<=i} W_ij phi(q_i).phi(k_j)]
+    with W = decay_matrix(a): the [SLA] Knowl 3 masked form with the causal
+    mask replaced by the compounded decays ([HN]).  q, k: [..., N, d_k];
+    v: [..., N, d_v]; a: [..., N].
+    """
+    fq = feature_map(q, fmap)
+    fk = feature_map(k, fmap)
+    v = _f64(v)
+    w = (fq @ np.swapaxes(fk, -1, -2)) * decay_matrix(a)
+    num = w @ v
+    if not normalize:
+        return num
+    return num / w.sum(axis=-1)[..., None]
+
+
+def gated_decode_step(q, k, v, a, S, z, fmap: str, normalize=True):
+    """One gated step: S' = a S + phi(k)^T v, z' = a z + phi(k)^T, then the read
+    phi(q) S' [/ phi(q) z'].  Returns (y, S', z'); the inputs are not modified.
+
+    q, k: [..., d_k]; v: [..., d_v]; a: [...]; S: [..., D, d_v]; z: [..., D].
+    """
+    fq = feature_map(q, fmap)
+    fk = feature_map(k, fmap)
+    v = _f64(v)
+    a = _f64(a)
+    S_new = a[..., None, None] * _f64(S) + fk[..., :, None] * v[..., None, :]
+    z_new = a[..., None] * _f64(z) + fk
+    num = np.einsum("...r,...rc->...c", fq, S_new)
+    if not normalize:
+        return num, S_new, z_new
+    den = np.einsum("...r,...r->...", fq, z_new)
+    return num / den[..., None], S_new, z_new
+
+
+def attention_gated_recurrent(q, k, v, a, fmap: str, S0=None, z0=None,
+                              normalize=True):
+    """The gated recurrence over all N positions; returns (y, S_N, z_N).
+
+    The state starts at zero unless (S0, z0) is given (it is then decayed by
+    a_1 before token 1 is added, like any earlier state).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    a = _f64(a)
+    batch = q.shape[:-2]
+    n = q.shape[-2]
+    D = feature_dim(fmap, q.shape[-1])
+    dv = v.shape[-1]
+    S = np.zeros(batch + (D, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros(batch + (D,)) if z0 is None else _f64(z0).copy()
+    y = np.empty(batch + (n, dv), dtype=np.float64)
+    for t in range(n):
+        y[..., t, :], S, z = gated_decode_step(q[..., t, :], k[..., t, :],
+                                               v[..., t, :], a[..., t], S, z,
+                                               fmap, normalize)
+    return y, S, z
+
+
+def _suffix_products(a) -> np.ndarray:
+    """P[..., j] = a_{j+1} ... a_N (1 for j = N): the weight of token j in the
+    state after the last token.  Explicit running products, last to first."""
+    a = _f64(a)
+    n = a.shape[-1]
+    P = np.empty(a.shape, dtype=np.float64)
+    run = np.ones(a.shape[:-1], dtype=np.float64)
+    for j in range(n - 1, -1, -1):
+        P[..., j] = run
+        run = run * a[..., j]
+    return P
+
+
+def gated_final_state(k, v, a, fmap: str, S0=None, z0=None):
+    """State after N gated tokens, summed in closed form:
+    S_N = sum_j (a_{j+1} ... a_N) phi(k_j)^T v_j + (a_1 ... a_N) S0, and the same
+    for z with v replaced by 1."""
+    fk = feature_map(k, fmap)
+    v = _f64(v)
+    P = _suffix_products(a)                                  # [..., N]
+    S = np.swapaxes(fk * P[..., None], -1, -2) @ v
+    z = (fk * P[..., None]).sum(axis=-2)
+    if S0 is not None:
+        total = np.prod(_f64(a), axis=-1)
+        S = S + total[..., None, None] * _f64(S0)
+        z = z + total[..., None] * _f64(z0)
+    return S, z
+
+
+def attention_gated_rows(q, k, v, a, fmap: str, rows, normalize=True) -> np.ndarray:
+    """The gated definition at the (0-based) positions `rows` of ONE sequence
+    and head (q, k: [N, d_k], v: [N, d_v], a: [N]); any N.  Row t weighs
+    token j <= t by a_{j+1} ... a_t."""
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    a = _f64(a)
+    out = np.empty((len(rows), v.shape[-1]), dtype=np.float64)
+    for r, t in enumerate(rows):
+        fq = feature_map(q[t], fmap)
+        fk = feature_map(k[: t + 1], fmap)
+        w = (fk @ fq) * _suffix_products(a[: t + 1])
+        out[r] = w @ v[: t + 1]
+        if normalize:
+            out[r] /= w.sum()
+    return out
 
 
 def kernel_value(q, k, fmap: str) -> np.ndarray:

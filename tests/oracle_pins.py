@@ -19,6 +19,13 @@ recall-throughput tradeoff" = SLA; "Transformers are RNNs ..." = TR):
                    d' = 16), the Knowl 3 identity, hand-written features,
                    and the fold relation to the ordered-pair state
   elu_torch        torch.nn.functional.elu(x) + 1 (a library routine)
+  gated_*          the scalar-decay form (the gated recurrence and the
+                   scalar-transition duality in the Hacker News comments on
+                   "Transformers are RNNs" = HN): exact rational brute force
+                   with the decay products multiplied out, scipy's IIR filter
+                   for a constant decay, a reset (a_t = 0) cutting the past
+                   off, a = 0 and a = 1 as closed forms, continuation through
+                   a state, and the final state summed three ways
   closed forms     first token, constant key, zero Taylor query, constant v,
                    linearity in v, convex hull, positivity, final state,
                    decode continuation, sampled rows, hand-worked golden file
@@ -395,6 +402,191 @@ def pin_golden_handworked(o):
         assert _rel(S, S_want) < 1e-14 and _rel(z, z_want) < 1e-14
 
 
+# ----------------------------------------------------------- gated form ----
+def _exact_gated(fmap, q, k, v, a, normalize):
+    """HN gated recurrence unrolled, exactly: token j's weight at position i
+    is the product a_{j+1} ... a_i, multiplied out factor by factor."""
+    n, dv = len(q), len(v[0])
+    out = []
+    for i in range(n):
+        w = []
+        for j in range(i + 1):
+            c = Fraction(1)
+            for t in range(j + 1, i + 1):
+                c *= a[t]
+            kv = (_exact_kernel_sym(q[i], k[j]) if fmap == "taylor2sym"
+                  else _exact_kernel(fmap, q[i], k[j]))
+            w.append(c * kv)
+        num = [sum(w[j] * v[j][col] for j in range(i + 1)) for col in range(dv)]
+        if normalize:
+            den = sum(w)
+            num = [x / den for x in num]
+        out.append(num)
+    return out
+
+
+_GATES = [Fraction(0), Fraction(1, 4), Fraction(1, 2), Fraction(2, 3), Fraction(1)]
+
+
+def _check_exact_gated(o, fmap, nonneg):
+    for seed, (n, dk, dv) in enumerate([(1, 1, 1), (6, 2, 3), (11, 3, 2)]):
+        q, k, v = _rational_inputs(200 + seed, n, dk, dv, nonneg)
+        r = _rng(300 + seed)
+        a = [_GATES[int(r.integers(0, len(_GATES)))] for _ in range(n)]
+        if n > 4:
+            a[4] = Fraction(0)       # at least one reset
+            a[2] = Fraction(2, 3)    # and one partial decay
+        qf, kf, vf = _as_f64(q), _as_f64(k), _as_f64(v)
+        af = np.array([float(x) for x in a])
+        for normalize in (True, False):
+            want = _as_f64(_exact_gated(fmap, q, k, v, a, normalize))
+            got_q = o.attention_gated_quadratic(qf, kf, vf, af, fmap, normalize)
+            got_r = o.attention_gated_recurrent(qf, kf, vf, af, fmap,
+                                                normalize=normalize)[0]
+            got_rows = o.attention_gated_rows(qf, kf, vf, af, fmap, list(range(n)),
+                                              normalize)
+            for got in (got_q, got_r, got_rows):
+                assert _rel(got, want) < 1e-13, (fmap, n, normalize)
+        if fmap == "elu1":
+            # ELU1 on non-negative rationals: phi(k) = k + 1, so the final
+            # state is exact too
+            S_want = [[sum(_prod(a[j + 1:]) * (k[j][r_] + 1) * v[j][c]
+                           for j in range(n)) for c in range(dv)] for r_ in range(dk)]
+            z_want = [sum(_prod(a[j + 1:]) * (k[j][r_] + 1) for j in range(n))
+                      for r_ in range(dk)]
+            _, S, z = o.attention_gated_recurrent(qf, kf, vf, af, fmap)
+            S2, z2 = o.gated_final_state(kf, vf, af, fmap)
+            for SS, zz in ((S, z), (S2, z2)):
+                assert _rel(SS, _as_f64(S_want)) < 1e-13
+                assert _rel(zz, np.array([float(x) for x in z_want])) < 1e-13
+
+
+def _prod(xs):
+    p = Fraction(1)
+    for x in xs:
+        p *= x
+    return p
+
+
+def pin_gated_exact_elu1(o):
+    _check_exact_gated(o, "elu1", nonneg=True)
+
+
+def pin_gated_exact_taylor(o):
+    _check_exact_gated(o, "taylor2", nonneg=False)
+    _check_exact_gated(o, "taylor2sym", nonneg=False)
+
+
+def pin_gated_iir_filter(o):
+    """Constant decay alpha and a constant key: the decayed sums are the
+    first-order recursive filter y_n = alpha y_{n-1} + x_n, which scipy's
+    lfilter([1], [1, -alpha]) computes; the normalised output is the
+    filtered v over the filtered ones."""
+    from scipy.signal import lfilter
+    r = _rng(21)
+    for fmap in ("elu1", "taylor2", "taylor2sym"):
+        for alpha in (0.0, 0.37, 0.9, 1.0):
+            n = 50
+            q = r.standard_normal((n, 3))
+            k = np.tile(r.standard_normal((1, 3)), (n, 1))
+            v = r.standard_normal((n, 4))
+            a = np.full(n, alpha)
+            fv = lfilter([1.0], [1.0, -alpha], v, axis=0)
+            f1 = lfilter([1.0], [1.0, -alpha], np.ones(n))
+            y = o.attention_gated_recurrent(q, k, v, a, fmap)[0]
+            assert _rel(y, fv / f1[:, None]) < 1e-12, (fmap, alpha)
+            y = o.attention_gated_quadratic(q, k, v, a, fmap)
+            assert _rel(y, fv / f1[:, None]) < 1e-12, (fmap, alpha)
+            kq = o.kernel_value(q, k, fmap)
+            y_un = o.attention_gated_recurrent(q, k, v, a, fmap, normalize=False)[0]
+            assert _rel(y_un, kq[:, None] * fv) < 1e-12, (fmap, alpha)
+            _, S, z = o.attention_gated_recurrent(q, k, v, a, fmap)
+            fk = o.feature_map(k[0], fmap)
+            assert _rel(S, np.outer(fk, fv[-1])) < 1e-12
+            assert _rel(z, fk * f1[-1]) < 1e-12
+
+
+def pin_gated_zero_and_one(o):
+    """a = 0 keeps only the current token: the normalised output is v_t and
+    the unnormalised one (phi(q_t).phi(k_t)) v_t, with the kernel value
+    computed without features (torch's elu, or 1 + s + s^2/2).  a = 1 is the
+    ungated recurrence."""
+    import torch
+    r = _rng(22)
+    q = r.standard_normal((2, 30, 4))
+    k = r.standard_normal((2, 30, 4))
+    v = r.standard_normal((2, 30, 5))
+    zero = np.zeros((2, 30))
+    one = np.ones((2, 30))
+    for fmap in ("elu1", "taylor2", "taylor2sym"):
+        if fmap == "elu1":
+            e = lambda x: torch.nn.functional.elu(torch.from_numpy(x)).numpy() + 1.0
+            kq = np.sum(e(q) * e(k), axis=-1)
+        else:
+            s_ = np.sum(q * k, axis=-1)
+            kq = 1.0 + s_ + 0.5 * s_ * s_
+        for f in (o.attention_gated_quadratic,
+                  lambda *x, **kw: o.attention_gated_recurrent(*x, **kw)[0]):
+            assert _rel(f(q, k, v, zero, fmap), v) < 1e-14
+            assert _rel(f(q, k, v, zero, fmap, normalize=False), kq[..., None] * v) < 1e-13
+            assert _rel(f(q, k, v, one, fmap), o.attention_quadratic(q, k, v, fmap)) < 1e-12
+
+
+def pin_gated_reset_cuts_the_past(o):
+    """A reset a_r = 0 removes every token before r: from r on, outputs and
+    state equal a fresh run over the tail."""
+    r = _rng(23)
+    for fmap in ("elu1", "taylor2sym"):
+        q = r.standard_normal((3, 40, 4))
+        k = r.standard_normal((3, 40, 4))
+        v = r.standard_normal((3, 40, 2))
+        a = r.uniform(0.5, 1.0, (3, 40))
+        a[:, 17] = 0.0
+        for normalize in (True, False):
+            y, S, z = o.attention_gated_recurrent(q, k, v, a, fmap, normalize=normalize)
+            y2, S2, z2 = o.attention_gated_recurrent(q[:, 17:], k[:, 17:], v[:, 17:],
+                                                     a[:, 17:], fmap, normalize=normalize)
+            assert _rel(y[:, 17:], y2) < 1e-12
+            assert _rel(S, S2) < 1e-12 and _rel(z, z2) < 1e-12
+            yq = o.attention_gated_quadratic(q, k, v, a, fmap, normalize)
+            assert _rel(yq[:, 17:], y2) < 1e-12
+
+
+def pin_gated_continuation_and_state(o):
+    """Two runs joined through the state equal one run; the final state from
+    the recurrence, the closed form and a plain loop of decayed outer
+    products agree (with a start state)."""
+    r = _rng(24)
+    for fmap, dk, dv in (("elu1", 5, 3), ("taylor2", 3, 4), ("taylor2sym", 3, 4)):
+        q = r.standard_normal((2, 45, dk))
+        k = r.standard_normal((2, 45, dk))
+        v = r.standard_normal((2, 45, dv))
+        a = r.uniform(0.0, 1.0, (2, 45))
+        D = o.feature_dim(fmap, dk)
+        S0 = r.standard_normal((2, D, dv))
+        z0 = np.abs(r.standard_normal((2, D))) + 1.0
+        y_all, S_all, z_all = o.attention_gated_recurrent(q, k, v, a, fmap, S0, z0)
+        y_a, S_a, z_a = o.attention_gated_recurrent(q[:, :19], k[:, :19], v[:, :19],
+                                                    a[:, :19], fmap, S0, z0)
+        y_b, S_b, z_b = o.attention_gated_recurrent(q[:, 19:], k[:, 19:], v[:, 19:],
+                                                    a[:, 19:], fmap, S_a, z_a)
+        assert _rel(np.concatenate([y_a, y_b], axis=1), y_all) < 1e-12
+        assert _rel(S_b, S_all) < 1e-12 and _rel(z_b, z_all) < 1e-12
+        S2, z2 = o.gated_final_state(k, v, a, fmap, S0, z0)
+        assert _rel(S2, S_all) < 1e-12 and _rel(z2, z_all) < 1e-12
+        fk = o.feature_map(k, fmap)
+        S3, z3 = S0.copy(), z0.copy()
+        for t in range(45):
+            S3 = S3 * a[:, t, None, None] + np.einsum("br,bc->brc", fk[:, t], v[:, t])
+            z3 = z3 * a[:, t, None] + fk[:, t]
+        assert _rel(S3, S_all) < 1e-12 and _rel(z3, z_all) < 1e-12
+        rows = [0, 7, 44]
+        for b in range(2):
+            got = o.attention_gated_rows(q[b], k[b], v[b], a[b], fmap, rows)
+            want = o.attention_gated_recurrent(q[b], k[b], v[b], a[b], fmap)[0][rows]
+            assert _rel(got, want) < 1e-12
+
+
 PINS = [
     pin_exact_elu1,
     pin_exact_taylor2,
@@ -416,4 +608,10 @@ PINS = [
     pin_final_state,
     pin_decode_continuation,
     pin_golden_handworked,
+    pin_gated_exact_elu1,
+    pin_gated_exact_taylor,
+    pin_gated_iir_filter,
+    pin_gated_zero_and_one,
+    pin_gated_reset_cuts_the_past,
+    pin_gated_continuation_and_state,
 ]

@@ -185,12 +185,66 @@ def _m_sym_lower_order(o):
     o.phi_taylor2_sym = phi
 
 
+def _m_gated_decay_after_add(o):
+    # the new token decayed together with the old state
+    def step(q, k, v, a, S, z, fmap, normalize=True):
+        fq, fk = o.feature_map(q, fmap), o.feature_map(k, fmap)
+        a = np.asarray(a, dtype=np.float64)
+        S_new = a[..., None, None] * (S + fk[..., :, None] * np.asarray(v)[..., None, :])
+        z_new = a[..., None] * (z + fk)
+        num = np.einsum("...r,...rc->...c", fq, S_new)
+        if not normalize:
+            return num, S_new, z_new
+        return num / np.einsum("...r,...r->...", fq, z_new)[..., None], S_new, z_new
+    o.gated_decode_step = step
+
+
+def _m_gated_z_not_decayed(o):
+    def step(q, k, v, a, S, z, fmap, normalize=True):
+        fq, fk = o.feature_map(q, fmap), o.feature_map(k, fmap)
+        a = np.asarray(a, dtype=np.float64)
+        S_new = a[..., None, None] * S + fk[..., :, None] * np.asarray(v)[..., None, :]
+        z_new = z + fk
+        num = np.einsum("...r,...rc->...c", fq, S_new)
+        if not normalize:
+            return num, S_new, z_new
+        return num / np.einsum("...r,...r->...", fq, z_new)[..., None], S_new, z_new
+    o.gated_decode_step = step
+
+
+def _m_gated_matrix_own_factor(o):
+    # W_ij = a_j ... a_i: token j's own coefficient included
+    def W(a):
+        a = np.asarray(a, dtype=np.float64)
+        n = a.shape[-1]
+        out = np.zeros(a.shape[:-1] + (n, n))
+        for i in range(n):
+            for j in range(i + 1):
+                out[..., i, j] = np.prod(a[..., j:i + 1], axis=-1)
+        return out
+    o.decay_matrix = W
+
+
+def _m_gated_suffix_own_factor(o):
+    def P(a):
+        a = np.asarray(a, dtype=np.float64)
+        return np.flip(np.cumprod(np.flip(a, -1), axis=-1), -1)
+    o._suffix_products = P
+
+
+def _m_gated_normalize_ignored(o):
+    f = o.attention_gated_quadratic
+    o.attention_gated_quadratic = lambda q, k, v, a, fmap, normalize=True: f(q, k, v, a, fmap, True)
+
+
 MUTANTS = [
     _m_elu_no_exp, _m_elu_plain_exp, _m_elu_missing_plus_one,
     _m_taylor_no_sqrt2, _m_taylor_no_constant, _m_taylor_wrong_layout,
     _m_mask_strict, _m_no_mask, _m_read_before_update, _m_den_uses_key,
     _m_state_transposed, _m_rows_off_by_one, _m_value_sign,
     _m_sym_square_unscaled, _m_sym_pair_scaled, _m_sym_pair_doubled, _m_sym_lower_order,
+    _m_gated_decay_after_add, _m_gated_z_not_decayed, _m_gated_matrix_own_factor,
+    _m_gated_suffix_own_factor, _m_gated_normalize_ignored,
 ]
 
 
