@@ -136,18 +136,26 @@ bool plan_segments(int64_t BH, int64_t N, int64_t seg_len, int64_t row_bytes,
   return true;
 }
 
-size_t workspace_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nseg) {
-  if (nseg <= 1) return 0;
+// Workspace: BH * nseg slots of partial states, then one float per slot
+// (the log2 decay of a segment in gated calls), padded to 16 bytes.
+size_t slots_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nseg) {
   return (size_t)BH * (size_t)nseg * (size_t)slot_floats(map, dk, dv) * 4u;
 }
 
+size_t workspace_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nseg) {
+  if (nseg <= 1) return 0;
+  const size_t logs = ((size_t)BH * (size_t)nseg * 4u + 15u) & ~(size_t)15u;
+  return slots_bytes(map, BH, dk, dv, nseg) + logs;
+}
+
+template <bool GATED>
 hipError_t dispatch_prefill(int map, int dtype, int64_t dk, int64_t dv,
                             const PrefillArgs& a, hipStream_t st) {
   map = prefill_map(map);
-#define X(M, DK, DV)                                                     \
-  if (map == M && dk == DK && dv == DV)                                  \
-    return dtype == LINATTN_DTYPE_F32 ? launch_prefill<M, float, DK, DV>(a, st) \
-                                      : launch_prefill<M, bf16_t, DK, DV>(a, st);
+#define X(M, DK, DV)                                                            \
+  if (map == M && dk == DK && dv == DV)                                         \
+    return dtype == LINATTN_DTYPE_F32 ? launch_prefill<M, float, DK, DV, GATED>(a, st) \
+                                      : launch_prefill<M, bf16_t, DK, DV, GATED>(a, st);
   LINATTN_FOR_PREFILL_SHAPES(X)
 #undef X
   return hipErrorInvalidValue;
@@ -155,16 +163,149 @@ hipError_t dispatch_prefill(int map, int dtype, int64_t dk, int64_t dv,
 
 hipError_t dispatch_decode(int map, int dtype, int64_t dk, int64_t dv,
                            const void* q, const void* k, const void* v,
-                           float* S, float* z, void* y, int64_t BH,
-                           hipStream_t st) {
+                           const float* gate, int normalize, float* S, float* z,
+                           void* y, int64_t BH, hipStream_t st) {
 #define X(M, DK, DV)                                                            \
   if (map == M && dk == DK && dv == DV)                                         \
     return dtype == LINATTN_DTYPE_F32                                           \
-               ? launch_decode<M, float, DK, DV>(q, k, v, S, z, y, BH, st)      \
-               : launch_decode<M, bf16_t, DK, DV>(q, k, v, S, z, y, BH, st);
+               ? launch_decode<M, float, DK, DV>(q, k, v, gate, normalize, S, z, y, BH, st) \
+               : launch_decode<M, bf16_t, DK, DV>(q, k, v, gate, normalize, S, z, y, BH, st);
   LINATTN_FOR_SHAPES(X)
 #undef X
   return hipErrorInvalidValue;
+}
+
+linattn_status_t prefill_common(int map, int dtype, int64_t B, int64_t H,
+                                int64_t N, int64_t d_k, int64_t d_v,
+                                const void* q, const void* k, const void* v,
+                                bool gated, const float* gate, int normalize,
+                                void* y, const float* S_in, const float* z_in,
+                                float* S_out, float* z_out, int64_t seg_len,
+                                void* workspace, size_t workspace_bytes_given,
+                                void* stream) {
+  if (!valid_map(map) || !valid_dtype(dtype) || B <= 0 || H <= 0 || N <= 0 ||
+      d_k <= 0 || d_v <= 0)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!is_supported(map, dtype, d_k, d_v)) return LINATTN_ERR_UNSUPPORTED;
+  if (B > kMaxElems / H || N > kMaxElems / (B * H * (d_k > d_v ? d_k : d_v)))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  const int64_t BH = B * H;
+  if (BH > INT_MAX) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (q == nullptr || k == nullptr || v == nullptr || y == nullptr)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (gated && (gate == nullptr || !aligned4(gate) || (normalize != 0 && normalize != 1)))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if ((S_in && (!aligned4(S_in) || !aligned4(z_in))) ||
+      (S_out && (!aligned4(S_out) || !aligned4(z_out))))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  int nseg, seg_chunks;
+  const int64_t row_bytes = (d_k > d_v ? d_k : d_v) * (int64_t)elem_size(dtype);
+  if (!plan_segments(BH, N, seg_len, row_bytes, &nseg, &seg_chunks))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+
+  const size_t es = elem_size(dtype);
+  const int64_t D = feature_dim(map, d_k);
+  const Range rq = rng(q, BH * N * d_k, es), rk = rng(k, BH * N * d_k, es);
+  const Range rv = rng(v, BH * N * d_v, es), ry = rng(y, BH * N * d_v, es);
+  const Range rSi = rng(S_in, BH * D * d_v, 4), rzi = rng(z_in, BH * D, 4);
+  const Range rSo = rng(S_out, BH * D * d_v, 4), rzo = rng(z_out, BH * D, 4);
+  // outputs must not overlap inputs or each other (S_out == S_in and
+  // z_out == z_in exactly are allowed: in-place continuation)
+  const Range outs[3] = {ry, rSo, rzo};
+  const Range ins[3] = {rq, rk, rv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(outs[i], ins[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+  }
+  if (overlap(ry, rSi) || overlap(ry, rzi)) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (overlap(rSo, rSi) && S_out != S_in) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (overlap(rzo, rzi) && z_out != z_in) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (overlap(rSo, rzi) || overlap(rzo, rSi)) return LINATTN_ERR_INVALID_ARGUMENT;
+  const Range rg = rng(gated ? gate : nullptr, BH * N, 4);
+  for (int i = 0; i < 3; ++i)
+    if (overlap(outs[i], rg)) return LINATTN_ERR_INVALID_ARGUMENT;
+
+  const size_t need = workspace_bytes(map, BH, d_k, d_v, nseg);
+  if (need > 0) {
+    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes_given < need)
+      return LINATTN_ERR_WORKSPACE;
+    const Range rw{reinterpret_cast<const char*>(workspace), need};
+    const Range all[9] = {rq, rk, rv, ry, rSi, rzi, rSo, rzo, rg};
+    for (int i = 0; i < 9; ++i)
+      if (overlap(rw, all[i])) return LINATTN_ERR_INVALID_ARGUMENT;
+  }
+
+  PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.y = y;
+  a.S_in = S_in;
+  a.z_in = z_in;
+  a.S_out = S_out;
+  a.z_out = z_out;
+  a.ws = reinterpret_cast<float*>(workspace);
+  a.N = N;
+  a.BH = (int)BH;
+  a.nseg = nseg;
+  a.seg_chunks = seg_chunks;
+  a.prefix_mode = nseg == 1 ? 0 : (nseg <= kDirectPrefixMax ? 1 : 2);
+  a.sym = map == LINATTN_MAP_TAYLOR2_SYM ? 1 : 0;
+  a.gate = gated ? gate : nullptr;
+  a.ws_log = gated && nseg > 1
+                 ? a.ws + slots_bytes(map, BH, d_k, d_v, nseg) / sizeof(float)
+                 : nullptr;
+  a.normalize = gated ? normalize : 1;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = gated ? dispatch_prefill<true>(map, dtype, d_k, d_v, a, st)
+                             : dispatch_prefill<false>(map, dtype, d_k, d_v, a, st);
+  return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
+linattn_status_t decode_common(int map, int dtype, int64_t B, int64_t H,
+                               int64_t d_k, int64_t d_v, const void* q,
+                               const void* k, const void* v, bool gated,
+                               const float* gate, int normalize, float* S,
+                               float* z, void* y, void* stream) {
+  if (!valid_map(map) || !valid_dtype(dtype) || B <= 0 || H <= 0 || d_k <= 0 ||
+      d_v <= 0)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!is_supported(map, dtype, d_k, d_v)) return LINATTN_ERR_UNSUPPORTED;
+  if (B > kMaxElems / H) return LINATTN_ERR_INVALID_ARGUMENT;
+  const int64_t BH = B * H;
+  if (BH > INT_MAX) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (q == nullptr || k == nullptr || v == nullptr || S == nullptr || z == nullptr ||
+      y == nullptr)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (gated && (gate == nullptr || !aligned4(gate) || (normalize != 0 && normalize != 1)))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) ||
+      !aligned16(z) || !aligned16(y))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  const size_t es = elem_size(dtype);
+  const int64_t D = feature_dim(map, d_k);
+  const Range rq = rng(q, BH * d_k, es), rk = rng(k, BH * d_k, es);
+  const Range rv = rng(v, BH * d_v, es), ry = rng(y, BH * d_v, es);
+  const Range rS = rng(S, BH * D * d_v, 4), rz = rng(z, BH * D, 4);
+  const Range ins[3] = {rq, rk, rv};
+  const Range outs[3] = {ry, rS, rz};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(outs[i], ins[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (gated && overlap(outs[i], rng(gate, BH, 4))) return LINATTN_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = dispatch_decode(map, dtype, d_k, d_v, q, k, v,
+                                       gated ? gate : nullptr, gated ? normalize : 1,
+                                       S, z, y, BH, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
 }  // namespace
@@ -249,113 +390,39 @@ linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,
                                  float* S_out, float* z_out, int64_t seg_len,
                                  void* workspace, size_t workspace_bytes_given,
                                  void* stream) {
-  if (!valid_map(map) || !valid_dtype(dtype) || B <= 0 || H <= 0 || N <= 0 ||
-      d_k <= 0 || d_v <= 0)
-    return LINATTN_ERR_INVALID_ARGUMENT;
-  if (!is_supported(map, dtype, d_k, d_v)) return LINATTN_ERR_UNSUPPORTED;
-  if (B > kMaxElems / H || N > kMaxElems / (B * H * (d_k > d_v ? d_k : d_v)))
-    return LINATTN_ERR_INVALID_ARGUMENT;
-  const int64_t BH = B * H;
-  if (BH > INT_MAX) return LINATTN_ERR_INVALID_ARGUMENT;
-  if (q == nullptr || k == nullptr || v == nullptr || y == nullptr)
-    return LINATTN_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y))
-    return LINATTN_ERR_INVALID_ARGUMENT;
-  if ((S_in == nullptr) != (z_in == nullptr) || (S_out == nullptr) != (z_out == nullptr))
-    return LINATTN_ERR_INVALID_ARGUMENT;
-  if ((S_in && (!aligned4(S_in) || !aligned4(z_in))) ||
-      (S_out && (!aligned4(S_out) || !aligned4(z_out))))
-    return LINATTN_ERR_INVALID_ARGUMENT;
-  int nseg, seg_chunks;
-  const int64_t row_bytes = (d_k > d_v ? d_k : d_v) * (int64_t)elem_size(dtype);
-  if (!plan_segments(BH, N, seg_len, row_bytes, &nseg, &seg_chunks))
-    return LINATTN_ERR_INVALID_ARGUMENT;
+  return prefill_common(map, dtype, B, H, N, d_k, d_v, q, k, v, false, nullptr, 1,
+                        y, S_in, z_in, S_out, z_out, seg_len, workspace,
+                        workspace_bytes_given, stream);
+}
 
-  const size_t es = elem_size(dtype);
-  const int64_t D = feature_dim(map, d_k);
-  const Range rq = rng(q, BH * N * d_k, es), rk = rng(k, BH * N * d_k, es);
-  const Range rv = rng(v, BH * N * d_v, es), ry = rng(y, BH * N * d_v, es);
-  const Range rSi = rng(S_in, BH * D * d_v, 4), rzi = rng(z_in, BH * D, 4);
-  const Range rSo = rng(S_out, BH * D * d_v, 4), rzo = rng(z_out, BH * D, 4);
-  // outputs must not overlap inputs or each other (S_out == S_in and
-  // z_out == z_in exactly are allowed: in-place continuation)
-  const Range outs[3] = {ry, rSo, rzo};
-  const Range ins[3] = {rq, rk, rv};
-  for (int i = 0; i < 3; ++i) {
-    for (int j = 0; j < 3; ++j)
-      if (overlap(outs[i], ins[j])) return LINATTN_ERR_INVALID_ARGUMENT;
-    for (int j = i + 1; j < 3; ++j)
-      if (overlap(outs[i], outs[j])) return LINATTN_ERR_INVALID_ARGUMENT;
-  }
-  if (overlap(ry, rSi) || overlap(ry, rzi)) return LINATTN_ERR_INVALID_ARGUMENT;
-  if (overlap(rSo, rSi) && S_out != S_in) return LINATTN_ERR_INVALID_ARGUMENT;
-  if (overlap(rzo, rzi) && z_out != z_in) return LINATTN_ERR_INVALID_ARGUMENT;
-  if (overlap(rSo, rzi) || overlap(rzo, rSi)) return LINATTN_ERR_INVALID_ARGUMENT;
-
-  const size_t need = workspace_bytes(map, BH, d_k, d_v, nseg);
-  if (need > 0) {
-    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes_given < need)
-      return LINATTN_ERR_WORKSPACE;
-    const Range rw{reinterpret_cast<const char*>(workspace), need};
-    const Range all[8] = {rq, rk, rv, ry, rSi, rzi, rSo, rzo};
-    for (int i = 0; i < 8; ++i)
-      if (overlap(rw, all[i])) return LINATTN_ERR_INVALID_ARGUMENT;
-  }
-
-  PrefillArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.y = y;
-  a.S_in = S_in;
-  a.z_in = z_in;
-  a.S_out = S_out;
-  a.z_out = z_out;
-  a.ws = reinterpret_cast<float*>(workspace);
-  a.N = N;
-  a.BH = (int)BH;
-  a.nseg = nseg;
-  a.seg_chunks = seg_chunks;
-  a.prefix_mode = nseg == 1 ? 0 : (nseg <= kDirectPrefixMax ? 1 : 2);
-  a.sym = map == LINATTN_MAP_TAYLOR2_SYM ? 1 : 0;
-  const hipError_t e =
-      dispatch_prefill(map, dtype, d_k, d_v, a, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+linattn_status_t linattn_prefill_gated(int map, int dtype, int64_t B, int64_t H,
+                                       int64_t N, int64_t d_k, int64_t d_v,
+                                       const void* q, const void* k, const void* v,
+                                       const float* gate, int normalize, void* y,
+                                       const float* S_in, const float* z_in,
+                                       float* S_out, float* z_out, int64_t seg_len,
+                                       void* workspace, size_t workspace_bytes_given,
+                                       void* stream) {
+  return prefill_common(map, dtype, B, H, N, d_k, d_v, q, k, v, true, gate, normalize,
+                        y, S_in, z_in, S_out, z_out, seg_len, workspace,
+                        workspace_bytes_given, stream);
 }
 
 linattn_status_t linattn_decode_step(int map, int dtype, int64_t B, int64_t H,
                                      int64_t d_k, int64_t d_v, const void* q,
                                      const void* k, const void* v, float* S,
                                      float* z, void* y, void* stream) {
-  if (!valid_map(map) || !valid_dtype(dtype) || B <= 0 || H <= 0 || d_k <= 0 ||
-      d_v <= 0)
-    return LINATTN_ERR_INVALID_ARGUMENT;
-  if (!is_supported(map, dtype, d_k, d_v)) return LINATTN_ERR_UNSUPPORTED;
-  if (B > kMaxElems / H) return LINATTN_ERR_INVALID_ARGUMENT;
-  const int64_t BH = B * H;
-  if (BH > INT_MAX) return LINATTN_ERR_INVALID_ARGUMENT;
-  if (q == nullptr || k == nullptr || v == nullptr || S == nullptr || z == nullptr ||
-      y == nullptr)
-    return LINATTN_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(S) ||
-      !aligned16(z) || !aligned16(y))
-    return LINATTN_ERR_INVALID_ARGUMENT;
-  const size_t es = elem_size(dtype);
-  const int64_t D = feature_dim(map, d_k);
-  const Range rq = rng(q, BH * d_k, es), rk = rng(k, BH * d_k, es);
-  const Range rv = rng(v, BH * d_v, es), ry = rng(y, BH * d_v, es);
-  const Range rS = rng(S, BH * D * d_v, 4), rz = rng(z, BH * D, 4);
-  const Range ins[3] = {rq, rk, rv};
-  const Range outs[3] = {ry, rS, rz};
-  for (int i = 0; i < 3; ++i) {
-    for (int j = 0; j < 3; ++j)
-      if (overlap(outs[i], ins[j])) return LINATTN_ERR_INVALID_ARGUMENT;
-    for (int j = i + 1; j < 3; ++j)
-      if (overlap(outs[i], outs[j])) return LINATTN_ERR_INVALID_ARGUMENT;
-  }
-  const hipError_t e = dispatch_decode(map, dtype, d_k, d_v, q, k, v, S, z, y, BH,
-                                       reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+  return decode_common(map, dtype, B, H, d_k, d_v, q, k, v, false, nullptr, 1, S, z,
+                       y, stream);
+}
+
+linattn_status_t linattn_decode_step_gated(int map, int dtype, int64_t B, int64_t H,
+                                           int64_t d_k, int64_t d_v, const void* q,
+                                           const void* k, const void* v,
+                                           const float* gate, int normalize, float* S,
+                                           float* z, void* y, void* stream) {
+  return decode_common(map, dtype, B, H, d_k, d_v, q, k, v, true, gate, normalize, S,
+                       z, y, stream);
 }
 
 }  // extern "C"

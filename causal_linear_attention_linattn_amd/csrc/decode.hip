@@ -4,7 +4,13 @@
 // recall-throughput tradeoff", Knowl 3 recurrent equations; Knowl 5 second
 // paragraph): per sequence and head,
 //   S += phi(k)^T v,  z += phi(k)^T,  y = phi(q) S / phi(q) z
-// with the state updated before it is read.  Per step the whole state is
+// with the state updated before it is read.  The gated form (the gated
+// recurrence in the Hacker News discussion of "Transformers are RNNs", with a
+// scalar forget factor) first scales S and z by the step's coefficient a:
+//   S = a S + phi(k)^T v,  z = a z + phi(k)^T,
+// and may return the numerator phi(q) S unnormalised.  (a = 1 in the plain
+// form, where the scaling by exactly 1 changes no bit.)
+// Per step the whole state is
 // read once and written once, so the step is bound by HBM bandwidth; the
 // arithmetic (2 FMA per state element) is negligible.
 //
@@ -55,6 +61,8 @@ template <int MAP, typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v,
+                                                     const float* __restrict__ gate,
+                                                     int normalize,
                                                      float* __restrict__ S,
                                                      float* __restrict__ z,
                                                      T* __restrict__ y) {
@@ -98,6 +106,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
     zr[p] = r < D ? zb[r] : 0.0f;
   }
 
+  const float ga = gate != nullptr ? gate[bh] : 1.0f;
   if (tid < DK) {
     xq[tid] = E::to_f32(q[(size_t)bh * DK + tid]);
     xk[tid] = E::to_f32(k[(size_t)bh * DK + tid]);
@@ -119,10 +128,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
       const float a = fk[r];
       const float b = fq[r];
       float4 t = s[p];
-      t.x += a * vv.x;
-      t.y += a * vv.y;
-      t.z += a * vv.z;
-      t.w += a * vv.w;
+      t.x = fmaf(a, vv.x, t.x * ga);
+      t.y = fmaf(a, vv.y, t.y * ga);
+      t.z = fmaf(a, vv.z, t.z * ga);
+      t.w = fmaf(a, vv.w, t.w * ga);
       S4[r * CPR + c4] = t;
       acc.x += b * t.x;
       acc.y += b * t.y;
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
   for (int p = 0; p < NZ; ++p) {
     const int r = tid + 256 * p;
     if (r < D) {
-      const float zn = zr[p] + fk[r];
+      const float zn = fmaf(zr[p], ga, fk[r]);
       zb[r] = zn;
       dp += fq[r] * zn;
     }
@@ -165,7 +174,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
       n.w += red[w][tid].w;
     }
     const float den = dred[0] + dred[1] + dred[2] + dred[3];
-    const float rd = fast_rcp(den);
+    const float rd = normalize ? fast_rcp(den) : 1.0f;
     T* yp = y + (size_t)bh * DV + 4 * tid;
     if constexpr (sizeof(T) == 2) {
       *reinterpret_cast<uint2*>(yp) =
@@ -177,12 +186,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q,
 }
 
 template <int MAP, typename T, int DK, int DV>
-hipError_t launch_decode(const void* q, const void* k, const void* v, float* S,
-                         float* z, void* y, int64_t BH, hipStream_t st) {
+hipError_t launch_decode(const void* q, const void* k, const void* v,
+                         const float* gate, int normalize, float* S, float* z,
+                         void* y, int64_t BH, hipStream_t st) {
   hipLaunchKernelGGL((decode_kernel<MAP, T, DK, DV>), dim3((unsigned)BH),
                      dim3(256), 0, st, reinterpret_cast<const T*>(q),
                      reinterpret_cast<const T*>(k), reinterpret_cast<const T*>(v),
-                     S, z, reinterpret_cast<T*>(y));
+                     gate, normalize, S, z, reinterpret_cast<T*>(y));
   return hipGetLastError();
 }
 
@@ -237,11 +247,11 @@ hipError_t launch_feature_map(const void* x, int64_t rows, int d_k, float* phi,
 
 #define LINATTN_DECODE_INST(MAP, DK, DV)                                          \
   template hipError_t launch_decode<MAP, float, DK, DV>(                          \
-      const void*, const void*, const void*, float*, float*, void*, int64_t,      \
-      hipStream_t);                                                               \
+      const void*, const void*, const void*, const float*, int, float*, float*,   \
+      void*, int64_t, hipStream_t);                                               \
   template hipError_t launch_decode<MAP, bf16_t, DK, DV>(                         \
-      const void*, const void*, const void*, float*, float*, void*, int64_t,      \
-      hipStream_t);
+      const void*, const void*, const void*, const float*, int, float*, float*,   \
+      void*, int64_t, hipStream_t);
 
 LINATTN_DECODE_INST(MAP_ELU1, 16, 16)
 LINATTN_DECODE_INST(MAP_ELU1, 32, 32)

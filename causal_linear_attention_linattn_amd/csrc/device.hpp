@@ -79,6 +79,11 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r,
       uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
 }
 
+__device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r,
+                                                 uint32_t byte_offset) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_offset, 0, 0);
+}
+
 // elu(x) + 1 without a compare: exp(x) >= 1 + x for every x (convexity),
 // with equality only at 0, and exp(-|x|) <= 1 < 1 + x for x > 0, so
 //   phi(x) = max(1 + x, exp(-|x|))

@@ -3,7 +3,7 @@
 #include "prefill_impl.hpp"
 
 namespace linattn {
-#define X(DK, DV) template hipError_t launch_prefill<MAP_ELU1, bf16_t, DK, DV>(const PrefillArgs&, hipStream_t);
+#define X(DK, DV) template hipError_t launch_prefill<MAP_ELU1, bf16_t, DK, DV, false>(const PrefillArgs&, hipStream_t);
 X(16, 16) X(32, 32) X(64, 64)
 #undef X
 }  // namespace linattn

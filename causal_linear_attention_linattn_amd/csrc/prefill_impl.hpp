@@ -257,10 +257,13 @@ struct ChunkTiles {
   // O^T += V'^T A^T for key block jb2, where A^T = scores^T of the block's
   // keys against the wave's 16 queries (operands bq), kept where keep[] is
   // set (the causal mask); TAYLOR2 turns the raw q.k into 1 + s + s^2 / 2.
+  // GATED: each kept score is multiplied by its decay weight dec[] (the
+  // product of the coefficients after the key up to the query).
+  template <bool GATED = false>
   __device__ static __forceinline__ void within_chunk(const T* sK, const frag (&vf)[NCT - 1],
                                                       const frag (&bq)[SH::NKBS], const bool (&keep)[8],
                                                       const frag& ones, f32x4_t (&O)[NCT], int jb2,
-                                                      int lane) {
+                                                      int lane, const float* dec = nullptr) {
     const int i16 = lane & 15;
     f32x4_t sc[2];
 #pragma unroll
@@ -278,6 +281,7 @@ struct ChunkTiles {
         const float sv = sc[h][t];
         float val;
         if constexpr (MAP == MAP_ELU1) val = sv; else val = 1.0f + sv + 0.5f * sv * sv;
+        if constexpr (GATED) val *= dec[4 * h + t];
         f[4 * h + t] = keep[4 * h + t] ? val : 0.0f;
       }
     const frag bA = E::make(f);
@@ -294,6 +298,7 @@ struct Stage {
   uint4 k[NK];
   uint4 v[NV];
   uint4 q[SH::NQU];
+  float gt;  // gated form: decay coefficient of token (lane) of the chunk
 };
 
 template <int I, int N, class F>
@@ -304,7 +309,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int MAP, typename T, int DK, int DV, bool OUT>
+template <int MAP, typename T, int DK, int DV, bool OUT, bool GATED>
 __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   using SH = PrefillShape<MAP, T, DK, DV>;
   using E = Elem<T>;
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   constexpr int KT_EL = kNeedKT ? DK * CS : EPU;
   constexpr int V_EL = BF ? C * RTV::STRIDE : DV * CS;
   constexpr int S_EL = OUT ? SH::NCOL * PS : EPU;
-  constexpr int kTileBytes = 2 * (K_EL + KT_EL + V_EL) * (int)sizeof(T);
+  constexpr int kTileBytes = 2 * (K_EL + KT_EL + V_EL) * (int)sizeof(T) + (GATED ? 2 * C * 8 : 0);
   constexpr int NSB = kTileBytes + 2 * S_EL * (int)sizeof(T) <= 160 * 1024 ? 2 : 1;
   __shared__ __align__(16) T sK0[K_EL];
   __shared__ __align__(16) T sK1[K_EL];
@@ -341,6 +346,11 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   __shared__ __align__(16) T sV1[V_EL];
   __shared__ __align__(16) T sS0[S_EL];
   __shared__ __align__(16) T sS1[NSB == 2 ? S_EL : EPU];
+  // Gated form, per LDS copy: sG[b][i] = log2 of the decay accumulated from
+  // the chunk's last reset at or before token i (or from the chunk start)
+  // through token i; sL[b][i] = the index of that reset, or -1.
+  __shared__ __align__(16) float sG[2][GATED ? C : 1];
+  __shared__ __align__(16) int sL[2][GATED ? C : 1];
   auto sK = [&](int b) __attribute__((always_inline)) { return b ? sK1 : sK0; };
   auto sKT = [&](int b) __attribute__((always_inline)) { return b ? sKT1 : sKT0; };
   auto sV = [&](int b) __attribute__((always_inline)) { return b ? sV1 : sV0; };
@@ -370,6 +380,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   const auto rv = make_rsrc(vg, (uint32_t)ntok * DV * ES);
   T* yg = OUT ? reinterpret_cast<T*>(a.y) + ((size_t)bh * N + tok_begin) * DV : nullptr;
   const auto ry = make_rsrc(yg, OUT ? (uint32_t)ntok * DV * ES : 0u);
+  const auto rg = make_rsrc(GATED ? a.gate + (size_t)bh * N + tok_begin : nullptr,
+                            GATED ? (uint32_t)ntok * 4u : 0u);
 
   // ------------------------------------------------------------ state ----
   f32x4_t Sacc[SH::MAXRT][NCT];
@@ -400,10 +412,18 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     // and the slots past `seg` read as zero.  (Rows past NRT, which exist
     // only when NRT is not a multiple of the wave count, take an
     // out-of-range offset; those accumulators are never used.)
+    // Gated: the state entering segment j + 1 is the one entering segment j
+    // scaled by segment j's total decay, plus segment j's own sum; the
+    // log2 decays past `seg` read as 0 (factor 1).
     const auto rw = make_rsrc(a.ws + ((size_t)bh * a.nseg + 1) * SH::SLOT,
                               (uint32_t)seg * SH::SLOT * 4u);
+    const auto rl = make_rsrc(GATED ? a.ws_log + (size_t)bh * a.nseg + 1 : nullptr,
+                              GATED ? (uint32_t)seg * 4u : 0u);
 #pragma unroll
-    for (int j = 0; j < kDirectPrefixMax - 1; ++j)
+    for (int j = 0; j < kDirectPrefixMax - 1; ++j) {
+      float fj = 1.0f;
+      if constexpr (GATED)
+        fj = __builtin_amdgcn_exp2f(__uint_as_float(buffer_load4(rl, (uint32_t)j * 4u)));
 #pragma unroll
       for (int m = 0; m < SH::MAXRT; ++m) {
         const int rt = w + 4 * m;
@@ -411,9 +431,14 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
         for (int ct = 0; ct < NCT; ++ct) {
           const uint32_t off = rt < NRT ? ((uint32_t)j * SH::SLOT + ((rt * NCT + ct) * 64 + lane) * 4) * 4u
                                         : kOOB;
-          Sacc[m][ct] += __builtin_bit_cast(f32x4_t, buffer_load16(rw, off));
+          const f32x4_t t = __builtin_bit_cast(f32x4_t, buffer_load16(rw, off));
+          if constexpr (GATED)
+            Sacc[m][ct] = Sacc[m][ct] * fj + t;
+          else
+            Sacc[m][ct] += t;
         }
       }
+    }
   }
 
   // ones column of V' (and ones row of V'^T): lane column 0 of the last tile
@@ -484,6 +509,35 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
         for (int u = 0; u < SH::NQU; ++u)
           s.q[u] = buffer_load16(rq, (tq * DK + u * EPU) * ES);
       }
+    }
+    if constexpr (GATED) {
+      if (w == 0) s.gt = __uint_as_float(buffer_load4(rg, (cb + lane) * 4u));
+    }
+  };
+
+  // Gated form: the decay of chunk `chunk` from its ring slot into copy b.
+  // Wave 0 takes log2 of each coefficient (tokens past the segment end get
+  // 0, i.e. a = 1, and never count as resets) and runs a segmented
+  // inclusive scan over the 64 tokens: a reset restarts the sum.
+  auto stage_gate = [&](const St& s, int b, int chunk) __attribute__((always_inline)) {
+    if constexpr (GATED) {
+      if (w != 0) return;
+      const bool valid = chunk * C + lane < ntok;
+      const float lg = __builtin_amdgcn_logf(s.gt);
+      const bool reset = valid && !(lg >= kResetLog2);
+      float G = valid && !reset ? lg : 0.0f;
+      int L = reset ? lane : -1;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float Gp = __shfl_up(G, off, 64);
+        const int Lp = __shfl_up(L, off, 64);
+        if (lane >= off && L < 0) {
+          G += Gp;
+          L = Lp;
+        }
+      }
+      sG[b][lane] = G;
+      sL[b][lane] = L;
     }
   };
 
@@ -598,14 +652,30 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 
   // phi(K)^T operand for state row tile rt, key block jb2: lane (rho = i16,
   // g) slot t <-> feature 16 rt + rho, token 32 jb2 + 8 g + t.
-  auto kt_frag = [&](int b, int rt, int jb2) __attribute__((always_inline)) -> frag {
+  // GATED: slot t is scaled by u[t], the decay from its token to the chunk
+  // end.
+  auto kt_frag = [&](int b, int rt, int jb2, const float (&u)[8]) __attribute__((always_inline)) -> frag {
     const int col = 32 * jb2 + 8 * g;
     if constexpr (MAP == MAP_ELU1) {
       if (16 * rt >= DK) return E::zero();
+      frag r;
       if constexpr (BF)
-        return tokfrag_bf(sK(b), RTK::STRIDE, RTK::UPR - 1, col, 16 * rt);
+        r = tokfrag_bf(sK(b), RTK::STRIDE, RTK::UPR - 1, col, 16 * rt);
       else
-        return E::load8(sKT(b) + (16 * rt + i16) * CS + col);
+        r = E::load8(sKT(b) + (16 * rt + i16) * CS + col);
+      if constexpr (GATED) {
+        float f[8];
+        if constexpr (BF) {
+          unpack16<T>(__builtin_bit_cast(uint4, r), f);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) f[t] = r[t];
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) f[t] *= u[t];
+        r = E::make(f);
+      }
+      return r;
     } else {
       float f[8];
       if (rt < 16) {
@@ -624,6 +694,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
         E::load8f(sKT(b) + 15 * CS + col, fb);
 #pragma unroll
         for (int t = 0; t < 8; ++t) f[t] = i16 == 0 ? fb[t] : 0.0f;
+      }
+      if constexpr (GATED) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) f[t] *= u[t];
       }
       return E::make(f);
     }
@@ -683,6 +757,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) keep[jb2][e] = 32 * jb2 + 8 * g + e <= il;
 
+  // Gated segment-sum pass: log2 of the segment's total decay (-inf once a
+  // reset has been passed).
+  float seg_log = 0.0f;
+
   // One chunk, computed from LDS copy b and query set b: stage chunk c + 1
   // from ring slot `nx` into copy 1 - b, refill the slot with chunk c + P,
   // then the outputs (OUT) and the state update of chunk c.
@@ -692,7 +770,26 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 
     write_tiles(nx, 1 - b);
     take_q(nx, 1 - b);
+    stage_gate(nx, 1 - b, c + 1);
     issue(c + 1 + P, nx);
+
+    // Gated form: decays of this chunk.  Query il carries the state from
+    // before the chunk with factor fq (0 past a reset); the chunk as a whole
+    // scales the carried state by fc.
+    float Gq = 0.0f, Ge = 0.0f, fq = 1.0f, fc = 1.0f;
+    int Lq = -1, Le = -1;
+    if constexpr (GATED) {
+      Ge = sG[b][C - 1];
+      Le = sL[b][C - 1];
+      fc = Le >= 0 ? 0.0f : __builtin_amdgcn_exp2f(Ge);
+      if constexpr (OUT) {
+        Gq = sG[b][il];
+        Lq = sL[b][il];
+        fq = Lq >= 0 ? 0.0f : __builtin_amdgcn_exp2f(Gq);
+      } else {
+        seg_log = Le >= 0 ? -__builtin_inff() : seg_log + Ge;
+      }
+    }
 
     f32x4_t O[OUT ? NCT : 1];
     frag qraw = E::zero();
@@ -725,6 +822,16 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
           E::mma(O[ct], av, bq);
         }
       }
+      if constexpr (GATED) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) O[ct] *= fq;
+      }
+    }
+    if constexpr (GATED) {
+#pragma unroll
+      for (int m = 0; m < SH::MAXRT; ++m)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) Sacc[m][ct] *= fc;
     }
 
     // Scheduling hint: interleave the staging arithmetic of chunk c + 1 (phi
@@ -749,6 +856,23 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
       for (int ct = 0; ct < NCT - 1; ++ct) vf[ct] = v_frag(b, jb2, ct);
 
+      // Gated form: weight of key 32 jb2 + 8 g + e at query il (dec) and at
+      // the chunk end (u); zero across a reset, and u is zero for tokens past
+      // the segment end so that they add nothing to the state.
+      float dec[8], u[8];
+      if constexpr (GATED) {
+        const float4 g0 = *reinterpret_cast<const float4*>(&sG[b][32 * jb2 + 8 * g]);
+        const float4 g1 = *reinterpret_cast<const float4*>(&sG[b][32 * jb2 + 8 * g + 4]);
+        const float Gk[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = 32 * jb2 + 8 * g + e;
+          if constexpr (OUT)
+            dec[e] = keep[jb2][e] && key >= Lq ? __builtin_amdgcn_exp2f(Gq - Gk[e]) : 0.0f;
+          u[e] = key >= Le && cb + key < ntok ? __builtin_amdgcn_exp2f(Ge - Gk[e]) : 0.0f;
+        }
+      }
+
       if constexpr (OUT) {
         // within-chunk term: scores^T of this key block against the wave's
         // queries (key blocks wholly after them come out fully masked)
@@ -757,7 +881,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
         for (int kbs = 0; kbs < SH::NKBS; ++kbs) {
           if constexpr (MAP == MAP_ELU1) bq[kbs] = q_frag(b, kbs); else bq[kbs] = qraw;
         }
-        CT::within_chunk(sK(b), vf, bq, keep[jb2], ones, O, jb2, lane);
+        CT::template within_chunk<GATED>(sK(b), vf, bq, keep[jb2], ones, O, jb2, lane, dec);
       }
 
       // state update: S' += phi(K)^T V' for this wave's row tiles
@@ -765,7 +889,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       for (int m = 0; m < SH::MAXRT; ++m) {
         const int rt = w + 4 * m;
         if (rt >= NRT) continue;
-        const frag ak = kt_frag(b, rt, jb2);
+        const frag ak = kt_frag(b, rt, jb2, u);
 #pragma unroll
         for (int ct = 0; ct < NCT - 1; ++ct) E::mma(Sacc[m][ct], ak, vf[ct]);
         E::mma(Sacc[m][NCT - 1], ak, ones);
@@ -776,7 +900,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       // normalise and write y (query il of this chunk; rows past the
       // segment end fall outside the store range)
       const float den = __shfl(O[NCT - 1][0], i16, 64);
-      const float rden = fast_rcp(den);
+      const float rden = GATED && !a.normalize ? 1.0f : fast_rcp(den);
       const uint32_t yrow = ((uint32_t)(cb + il) * DV + 4 * g) * ES;
 #pragma unroll
       for (int ct = 0; ct < NCT - 1; ++ct) {
@@ -805,6 +929,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   if constexpr (OUT) publish_state(0);
   write_tiles(st[0], 0);
   take_q(st[0], 0);
+  stage_gate(st[0], 0, 0);
   issue(P, st[0]);
   lds_barrier();
 
@@ -825,8 +950,9 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   // the empty chunks of the last trip) read k = 0 and v = 0: it added
   // nothing to the value columns and phi(0) to the z column.  Take that
   // back: phi(0) is 1 in every ELU1 feature, and in the TAYLOR2 constant
-  // feature (internal row 256) only.
-  {
+  // feature (internal row 256) only.  (The gated form gives those tokens
+  // weight 0 instead, so that a strongly decayed z is not left to cancel.)
+  if constexpr (!GATED) {
     const float n_pad = (float)(((nchunks + P - 1) / P) * P * C - ntok);
 #pragma unroll
     for (int m = 0; m < SH::MAXRT; ++m) {
@@ -863,13 +989,17 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) p[(rt * NCT + ct) * 64 + lane] = Sacc[m][ct];
     }
+    if constexpr (GATED) {
+      if (tid == 0) a.ws_log[(size_t)bh * a.nseg + seg + 1] = seg_log;
+    }
   }
 }
 
 // Exclusive prefix over segments, in place: slot s <- init + sum_{p<s} T_p,
 // where slot p+1 held segment p's sum T_p and init is the initial state.
-// Used when there are too many segments per head for each output workgroup
-// to add up its predecessors' sums itself.
+// Gated form: slot s <- 2^l_s slot(s-1) + T_(s-1), with l_s the log2 decay of
+// segment s - 1 (ws_log).  Used when there are too many segments per head for
+// each output workgroup to add up its predecessors' sums itself.
 template <int MAP, int DK, int DV>
 __global__ __launch_bounds__(256) void seg_scan_kernel(PrefillArgs a) {
   using SS = StateShape<MAP, DK, DV>;
@@ -886,6 +1016,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(PrefillArgs a) {
                                     e4 % 64);
   }
   f32x4_t* p = reinterpret_cast<f32x4_t*>(a.ws + (size_t)bh * a.nseg * SS::SLOT) + e4;
+  const float* lg = a.ws_log != nullptr ? a.ws_log + (size_t)bh * a.nseg : nullptr;
   p[0] = run;
   // batches of 16 slots: all loads of a batch are in flight at once
   constexpr int kB = 16;
@@ -897,17 +1028,18 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < kB; ++j)
       if (s0 + j < a.nseg) {
+        if (lg != nullptr) run *= __builtin_amdgcn_exp2f(lg[s0 + j]);
         run += t[j];
         p[(size_t)(s0 + j) * Q] = run;
       }
   }
 }
 
-template <int MAP, typename T, int DK, int DV>
+template <int MAP, typename T, int DK, int DV, bool GATED>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   using SS = StateShape<MAP, DK, DV>;
   if (a.nseg > 1) {
-    hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, false>),
+    hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, false, GATED>),
                        dim3(a.BH * (a.nseg - 1)), dim3(256), 0, st, a);
     if (a.prefix_mode == 2) {
       const int64_t threads = (int64_t)a.BH * (SS::SLOT / 4);
@@ -916,7 +1048,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
                          st, a);
     }
   }
-  hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, true>),
+  hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, true, GATED>),
                      dim3(a.BH * a.nseg), dim3(256), 0, st, a);
   return hipGetLastError();
 }

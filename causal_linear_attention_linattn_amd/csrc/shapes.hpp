@@ -40,7 +40,18 @@ struct PrefillArgs {
                    // segment sums themselves; 2: a scan kernel runs first
   int sym;         // MAP_TAYLOR2 only: S_in/S_out use the unordered-pair
                    // layout (kSymD rows) instead of the ordered one
+  // Gated (scalar-decay) calls only: the decay coefficients a [BH, N], the
+  // read (1: decayed-sum ratio, 0: numerator only), and the per-slot log2
+  // decay of each segment in the workspace (after the slots).
+  const float* gate;
+  float* ws_log;
+  int normalize;
 };
+
+// Per-step decays below 2^kResetLog2 are treated as exact resets by the
+// gated prefill (the carried state is dropped rather than scaled by the
+// tiny factor): the difference is below 2^-64 relative.
+constexpr float kResetLog2 = -64.0f;
 
 template <int MAP, int DK, int DV>
 struct StateShape {
@@ -57,13 +68,15 @@ struct StateShape {
   static_assert(DK % 16 == 0 && DV % 16 == 0, "d_k, d_v multiples of 16");
 };
 
-template <int MAP, typename T, int DK, int DV>
+template <int MAP, typename T, int DK, int DV, bool GATED>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 
+// gate: NULL for the plain recurrence, else one decay per (batch, head);
+// normalize as in PrefillArgs (gated calls only).
 template <int MAP, typename T, int DK, int DV>
 hipError_t launch_decode(const void* q, const void* k, const void* v,
-                         float* S, float* z, void* y, int64_t BH,
-                         hipStream_t st);
+                         const float* gate, int normalize, float* S, float* z,
+                         void* y, int64_t BH, hipStream_t st);
 
 template <int MAP, typename T>
 hipError_t launch_feature_map(const void* x, int64_t rows, int d_k,

@@ -9,6 +9,8 @@ Entry points (same names as the C ABI in include/linattn.h):
     feature_map(x, fmap)                      -> phi(x) float32 [..., D]
     prefill(q, k, v, fmap, state=None, ...)   -> y (and the final state)
     decode_step(q, k, v, S, z, fmap)          -> y; S, z updated in place
+    prefill_gated(q, k, v, gate, fmap, ...)   -> y (and the final state)
+    decode_step_gated(q, k, v, gate, S, z, fmap) -> y; S, z updated in place
 """
 from __future__ import annotations
 
@@ -66,6 +68,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.linattn_decode_step.argtypes = [i32, i32, i64, i64, i64, i64, vp, vp, vp,
                                       fp, fp, vp, vp]
     L.linattn_decode_step.restype = i32
+    L.linattn_prefill_gated.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp,
+                                        fp, i32, vp, fp, fp, fp, fp, i64, vp, sz, vp]
+    L.linattn_prefill_gated.restype = i32
+    L.linattn_decode_step_gated.argtypes = [i32, i32, i64, i64, i64, i64, vp, vp, vp,
+                                            fp, i32, fp, fp, vp, vp]
+    L.linattn_decode_step_gated.restype = i32
     _lib = L
     return L
 
@@ -147,6 +155,18 @@ def prefill(q, k, v, fmap: str, *, state=None, return_state=False,
     from.  return_state: also return the final (S, z).  seg_len: tokens per
     workgroup segment (0 = library choice, else a multiple of 64).
     """
+    return _prefill(q, k, v, None, True, fmap, state, return_state, seg_len, out)
+
+
+def prefill_gated(q, k, v, gate, fmap: str, *, normalize=True, state=None,
+                  return_state=False, seg_len: int = 0, out=None):
+    """Gated (scalar-decay) prefill: gate is float32 [B, H, N] holding a_t;
+    S_t = a_t S_{t-1} + phi(k_t)^T v_t (and z).  normalize=False returns the
+    numerator phi(q_t) S_t.  Other arguments as prefill()."""
+    return _prefill(q, k, v, gate, normalize, fmap, state, return_state, seg_len, out)
+
+
+def _prefill(q, k, v, gate, normalize, fmap, state, return_state, seg_len, out):
     L = load_library()
     _need_cuda(q, k, v)
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
@@ -172,10 +192,20 @@ def prefill(q, k, v, fmap: str, *, state=None, return_state=False,
         z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
     nws = workspace_bytes(fmap, q.dtype, B, H, N, d_k, d_v, seg_len)
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
-    _check(L.linattn_prefill(_map_id(fmap), _dtype_id(q), B, H, N, d_k, d_v,
-                             _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(S_in),
-                             _ptr(z_in), _ptr(S_out), _ptr(z_out), seg_len,
-                             _ptr(ws), nws, _stream(q)))
+    if gate is None:
+        _check(L.linattn_prefill(_map_id(fmap), _dtype_id(q), B, H, N, d_k, d_v,
+                                 _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(S_in),
+                                 _ptr(z_in), _ptr(S_out), _ptr(z_out), seg_len,
+                                 _ptr(ws), nws, _stream(q)))
+    else:
+        _need_cuda(gate)
+        if gate.dtype != torch.float32 or tuple(gate.shape) != (B, H, N):
+            raise ValueError("gate must be float32 [B, H, N]")
+        _check(L.linattn_prefill_gated(_map_id(fmap), _dtype_id(q), B, H, N, d_k, d_v,
+                                       _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                                       1 if normalize else 0, _ptr(y), _ptr(S_in),
+                                       _ptr(z_in), _ptr(S_out), _ptr(z_out), seg_len,
+                                       _ptr(ws), nws, _stream(q)))
     if return_state:
         return y, (S_out, z_out)
     return y
@@ -183,6 +213,16 @@ def prefill(q, k, v, fmap: str, *, state=None, return_state=False,
 
 def decode_step(q, k, v, S, z, fmap: str, *, out=None):
     """One generation step; q, k [B,H,d_k], v [B,H,d_v].  S, z updated in place."""
+    return _decode(q, k, v, None, True, S, z, fmap, out)
+
+
+def decode_step_gated(q, k, v, gate, S, z, fmap: str, *, normalize=True, out=None):
+    """One gated step: S = a S + phi(k)^T v, z = a z + phi(k)^T with gate
+    float32 [B, H] holding a; then the read as in prefill_gated."""
+    return _decode(q, k, v, gate, normalize, S, z, fmap, out)
+
+
+def _decode(q, k, v, gate, normalize, S, z, fmap, out):
     L = load_library()
     _need_cuda(q, k, v, S, z)
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
@@ -195,9 +235,18 @@ def decode_step(q, k, v, S, z, fmap: str, *, out=None):
     if tuple(S.shape) != (B, H, D, d_v) or tuple(z.shape) != (B, H, D):
         raise ValueError("state shapes must be [B,H,D,d_v] and [B,H,D]")
     y = out if out is not None else torch.empty_like(v)
-    _check(L.linattn_decode_step(_map_id(fmap), _dtype_id(q), B, H, d_k, d_v,
-                                 _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
-                                 _ptr(y), _stream(q)))
+    if gate is None:
+        _check(L.linattn_decode_step(_map_id(fmap), _dtype_id(q), B, H, d_k, d_v,
+                                     _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
+                                     _ptr(y), _stream(q)))
+    else:
+        _need_cuda(gate)
+        if gate.dtype != torch.float32 or tuple(gate.shape) != (B, H):
+            raise ValueError("gate must be float32 [B, H]")
+        _check(L.linattn_decode_step_gated(_map_id(fmap), _dtype_id(q), B, H, d_k, d_v,
+                                           _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                                           1 if normalize else 0, _ptr(S), _ptr(z),
+                                           _ptr(y), _stream(q)))
     return y
 
 

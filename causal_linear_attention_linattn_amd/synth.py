@@ -101,6 +101,17 @@ def draw_qkv(B, H, N, d_k, d_v, seed, *, dtype="bf16", qk_scale=1.0,
     return _store(q, dtype), _store(k, dtype), _store(v, dtype)
 
 
+def draw_gate(B, H, N, seed, *, lo=0.8, hi=1.0, reset_p=0.0, stream=2):
+    """Decay coefficients a [B, H, N] (float32): uniform on [lo, hi), and
+    exactly 0 with probability reset_p.  The pages give no distribution for
+    them; this spans mild decay, strong decay and resets."""
+    rng = np.random.Generator(np.random.PCG64([int(seed), int(stream)]))
+    a = rng.uniform(lo, hi, size=(B, H, N))
+    if reset_p > 0.0:
+        a = np.where(rng.uniform(size=(B, H, N)) < reset_p, 0.0, a)
+    return a.astype(np.float32)
+
+
 def workload_inputs(name, seed=0, **override):
     """Inputs of a named workload (shape overrides allowed for small cases).
 

@@ -107,9 +107,9 @@ linattn_status_t linattn_feature_map(int map, int dtype, const void* x,
                                      void* stream);
 
 /*
- * Bytes of device workspace linattn_prefill needs for this shape and
- * segment length (0 = the library's choice).  May be 0.  Returns (size_t)-1
- * for invalid or unsupported arguments.
+ * Bytes of device workspace linattn_prefill and linattn_prefill_gated need
+ * for this shape and segment length (0 = the library's choice).  May be 0.
+ * Returns (size_t)-1 for invalid or unsupported arguments.
  */
 size_t linattn_prefill_workspace_bytes(int map, int dtype, int64_t B,
                                        int64_t H, int64_t N, int64_t d_k,
@@ -150,6 +150,40 @@ linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * Gated (scalar-decay) causal prefill.  The state is scaled by a per-token
+ * coefficient a_t before the token is added (the gated linear recurrences
+ * of the Hacker News discussion of "Transformers are RNNs", "In the
+ * conversation": a forget factor that is a scalar times the identity, which
+ * the same discussion relates to state-space layers with scalar
+ * transitions through compounded coefficients a_1 ... a_t):
+ *     S_t = a_t S_{t-1} + phi(k_t)^T v_t,   z_t = a_t z_{t-1} + phi(k_t)^T,
+ *     y_t = phi(q_t) S_t / phi(q_t) z_t   (normalize = 1)
+ *     y_t = phi(q_t) S_t                  (normalize = 0).
+ * Unrolled, token j counts at position i with weight a_{j+1} ... a_i.
+ *   gate  [B, H, N] float32 device pointer, 4-byte aligned: a_t, meant to lie
+ *         in [0, 1] (a = 1 everywhere is the plain prefill; a = 0 drops all
+ *         earlier tokens and the initial state).  Coefficients below 2^-64
+ *         are taken as exactly 0 (a change below 2^-64 relative).  Values
+ *         outside [0, 1] are not checked: they are used as given (> 1
+ *         grows the state), and NaN or negative values give unspecified
+ *         outputs.  Never written; must not overlap y, S_out or z_out.
+ *   normalize  1 or 0 as above; anything else is an invalid argument.
+ * Every other argument, the workspace and the supported shapes are those of
+ * linattn_prefill; S_in (if given) is decayed by a_1 like any earlier state.
+ * The weights are formed in float32 as 2^(G_i - G_j) from running sums G of
+ * log2 a_t within each 64-token chunk, so the relative error of a weight
+ * grows with the magnitude of those sums (about 1e-5 for |G| <= 100).
+ */
+linattn_status_t linattn_prefill_gated(int map, int dtype, int64_t B, int64_t H,
+                                       int64_t N, int64_t d_k, int64_t d_v,
+                                       const void* q, const void* k, const void* v,
+                                       const float* gate, int normalize, void* y,
+                                       const float* S_in, const float* z_in,
+                                       float* S_out, float* z_out, int64_t seg_len,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/*
  * One generation step for all B*H sequences: update the state with the new
  * token, then read it ("Simple linear attention ...", Knowl 3 recurrent
  * equations; Knowl 5, second paragraph):
@@ -165,6 +199,20 @@ linattn_status_t linattn_decode_step(int map, int dtype, int64_t B, int64_t H,
                                      int64_t d_k, int64_t d_v, const void* q,
                                      const void* k, const void* v, float* S,
                                      float* z, void* y, void* stream);
+
+/*
+ * One gated generation step (the recurrence of linattn_prefill_gated):
+ *   S = a S + phi(k)^T v;  z = a z + phi(k)^T;  y = phi(q) S [/ phi(q) z].
+ *   gate [B, H] float32 device pointer, 4-byte aligned: this step's a per
+ *        sequence and head, used exactly as given (no 2^-64 cut-off here).
+ *   normalize 1 (ratio) or 0 (numerator only).
+ * Otherwise as linattn_decode_step; gate must not overlap y, S or z.
+ */
+linattn_status_t linattn_decode_step_gated(int map, int dtype, int64_t B, int64_t H,
+                                           int64_t d_k, int64_t d_v, const void* q,
+                                           const void* k, const void* v,
+                                           const float* gate, int normalize, float* S,
+                                           float* z, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -92,16 +92,19 @@ def test_workspace_bytes(lib):
     # one segment per head -> no workspace
     assert f(0, 1, 1, 2, 256, 16, 16, 0) == 0
     assert f(0, 1, 64, 64, 4096, 64, 64, 0) == 0
-    # explicit segments: B*H*nseg slots of NRT*NCT*256 floats
+    # explicit segments: B*H*nseg slots of NRT*NCT*256 floats, then one
+    # float per slot (a gated segment's log2 decay) padded to 16 bytes
+    def logs(n):
+        return (4 * n + 15) // 16 * 16
     slot_elu64 = 4 * 5 * 256
-    assert f(0, 1, 8, 8, 4096, 64, 64, 1024) == 64 * 4 * slot_elu64 * 4
+    assert f(0, 1, 8, 8, 4096, 64, 64, 1024) == 64 * 4 * slot_elu64 * 4 + logs(64 * 4)
     assert f(0, 1, 8, 8, 4096, 64, 64, 4096) == 0
     slot_tay = 18 * 5 * 256
-    assert f(1, 1, 8, 16, 2048, 16, 64, 512) == 128 * 4 * slot_tay * 4
+    assert f(1, 1, 8, 16, 2048, 16, 64, 512) == 128 * 4 * slot_tay * 4 + logs(128 * 4)
     # the unordered-pair map runs on the same kernels and workspace
-    assert f(2, 1, 8, 16, 2048, 16, 64, 512) == 128 * 4 * slot_tay * 4
+    assert f(2, 1, 8, 16, 2048, 16, 64, 512) == 128 * 4 * slot_tay * 4 + logs(128 * 4)
     # ragged: 65 tokens in 64-token segments -> 2 segments
-    assert f(0, 0, 1, 1, 65, 16, 16, 64) == 2 * (2 * 2 * 256) * 4
+    assert f(0, 0, 1, 1, 65, 16, 16, 64) == 2 * (2 * 2 * 256) * 4 + 16
     assert f(0, 1, 1, 1, 4096, 64, 64, 100) == bad     # not a multiple of 64
     assert f(0, 1, 1, 1, 0, 64, 64, 0) == bad
     assert f(0, 1, 1, 1, 64, 64, 32, 0) == bad         # unsupported
@@ -148,6 +151,36 @@ def test_prefill_validation_codes(lib):
     # S_out may equal S_in, but must not partially overlap it
     assert _prefill(lib, Si=A["Si"], zi=A["zi"], So=ctypes.c_void_p(0x50000010),
                     zo=A["zo"]) == INV
+
+
+def _prefill_gated(lib, gate=A["zi"], normalize=1, **kw):
+    a = dict(map=0, dtype=1, B=1, H=1, N=128, dk=64, dv=64, q=A["q"], k=A["k"],
+             v=A["v"], y=A["y"], Si=None, zi=None, So=None, zo=None, seg=0,
+             ws=None, wsb=0)
+    a.update(kw)
+    return lib.linattn_prefill_gated(a["map"], a["dtype"], a["B"], a["H"], a["N"],
+                                     a["dk"], a["dv"], a["q"], a["k"], a["v"], gate,
+                                     normalize, a["y"], a["Si"], a["zi"], a["So"],
+                                     a["zo"], a["seg"], a["ws"], a["wsb"], None)
+
+
+def test_gated_validation_codes(lib):
+    INV, UNS, WS = 1, 2, 3
+    assert _prefill_gated(lib, gate=None) == INV
+    assert _prefill_gated(lib, normalize=2) == INV
+    assert _prefill_gated(lib, gate=ctypes.c_void_p(0x60000002)) == INV   # misaligned
+    assert _prefill_gated(lib, gate=A["y"]) == INV                        # gate aliases y
+    assert _prefill_gated(lib, dk=48, dv=48) == UNS
+    assert _prefill_gated(lib, seg=64) == WS
+    # the workspace must not overlap the gate
+    assert _prefill_gated(lib, seg=64, ws=A["zi"], wsb=1 << 20) == INV
+    d = lib.linattn_decode_step_gated
+    args = (1, 1, 4, 16, 16, 64, A["q"], A["k"], A["v"])
+    assert d(*args, None, 1, A["Si"], A["zi"], A["y"], None) == INV
+    assert d(*args, A["So"], 3, A["Si"], A["zi"], A["y"], None) == INV
+    assert d(*args, A["y"], 1, A["Si"], A["zi"], A["y"], None) == INV   # gate aliases y
+    assert d(1, 1, 4, 16, 32, 64, A["q"], A["k"], A["v"], A["So"], 1, A["Si"], A["zi"],
+             A["y"], None) == UNS
 
 
 def test_decode_and_feature_map_validation(lib):

@@ -279,6 +279,147 @@ def test_decode_graph_replays_match_eager(fmap, d_k, d_v):
         assert torch.equal(S_g, S_e) and torch.equal(z_g, z_e), r
 
 
+# ------------------------------------------------------- gated form ------
+def _gate_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+@pytest.mark.parametrize("fmap,d_k,d_v", SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,seg_len", [(1, 0), (63, 0), (65, 64), (200, 64),
+                                       (517, 128), (700, 0)])
+def test_prefill_gated_small(fmap, d_k, d_v, dtype, N, seg_len):
+    """Gated prefill (a in [0.8, 1) with 2% resets) against the oracle's
+    gated recurrence, outputs and final state, ragged tails and segments."""
+    _log(f"prefill_gated {fmap} {d_k}x{d_v} {dtype} N={N} seg_len={seg_len}")
+    q, k, v = synth.draw_qkv(2, 3, N, d_k, d_v, seed=N, dtype=dtype,
+                             qk_scale=_qk_scale(fmap))
+    a = synth.draw_gate(2, 3, N, seed=N, reset_p=0.02)
+    y_ref, S_ref, z_ref = oracle.attention_gated_recurrent(q.f64(), k.f64(), v.f64(),
+                                                           a.astype(np.float64), fmap)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    y, (S, z) = ops.prefill_gated(qd, kd, vd, _gate_dev(a), fmap, return_state=True,
+                                  seg_len=seg_len)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert row_err(ops.to_numpy64(y), y_ref) <= tol
+    assert state_err(ops.to_numpy64(S), S_ref) <= tol
+    assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
+
+
+@pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64),
+                                         ("taylor2sym", 16, 32)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gate_kind", ["strong", "resets", "ones", "unnormalized"])
+def test_prefill_gated_regimes(fmap, d_k, d_v, dtype, gate_kind):
+    """Strong decay (a in [0, 0.5)), frequent resets, a = 1 (must equal the
+    plain prefill) and the unnormalised read, over many segments (the
+    scanned prefix) and a continuation from a state."""
+    _log(f"prefill_gated regime {gate_kind} {fmap} {dtype}")
+    B, H, N = 1, 4, 1000
+    q, k, v = synth.draw_qkv(B, H, N, d_k, d_v, seed=41, dtype=dtype,
+                             qk_scale=_qk_scale(fmap))
+    if gate_kind == "strong":
+        a = synth.draw_gate(B, H, N, seed=41, lo=0.0, hi=0.5)
+    elif gate_kind == "resets":
+        a = synth.draw_gate(B, H, N, seed=41, lo=0.9, hi=1.0, reset_p=0.1)
+    elif gate_kind == "ones":
+        a = np.ones((B, H, N), dtype=np.float32)
+    else:
+        a = synth.draw_gate(B, H, N, seed=41, lo=0.95, hi=1.0, reset_p=0.01)
+    normalize = gate_kind != "unnormalized"
+    a64 = a.astype(np.float64)
+    y_ref, S_ref, z_ref = oracle.attention_gated_recurrent(q.f64(), k.f64(), v.f64(),
+                                                           a64, fmap, normalize=normalize)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    ad = _gate_dev(a)
+    tol = TOL[dtype]
+    for seg_len in (0, 64, 192):
+        y, (S, z) = ops.prefill_gated(qd, kd, vd, ad, fmap, normalize=normalize,
+                                      return_state=True, seg_len=seg_len)
+        torch.cuda.synchronize()
+        assert row_err(ops.to_numpy64(y), y_ref) <= tol, seg_len
+        assert state_err(ops.to_numpy64(S), S_ref) <= tol, seg_len
+        assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol, seg_len
+    if gate_kind == "ones":
+        y_plain = ops.prefill(qd, kd, vd, fmap, seg_len=64)
+        y_g = ops.prefill_gated(qd, kd, vd, ad, fmap, seg_len=64)
+        torch.cuda.synchronize()
+        assert row_err(ops.to_numpy64(y_g), ops.to_numpy64(y_plain)) <= 1e-5
+    # continuation through a state: prefix 0..n1, then the rest
+    n1 = 321
+    sl = lambda x, lo, hi: x[:, :, lo:hi].contiguous()
+    _, st = ops.prefill_gated(sl(qd, 0, n1), sl(kd, 0, n1), sl(vd, 0, n1),
+                              ad[:, :, :n1].contiguous(), fmap, normalize=normalize,
+                              return_state=True)
+    y2, (S2, _) = ops.prefill_gated(sl(qd, n1, N), sl(kd, n1, N), sl(vd, n1, N),
+                                    ad[:, :, n1:].contiguous(), fmap, normalize=normalize,
+                                    state=st, return_state=True, seg_len=64)
+    torch.cuda.synchronize()
+    assert row_err(ops.to_numpy64(y2), y_ref[:, :, n1:]) <= tol
+    assert state_err(ops.to_numpy64(S2), S_ref) <= tol
+
+
+@pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64),
+                                         ("taylor2sym", 16, 64)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("normalize", [True, False])
+def test_decode_gated_from_oracle_state(fmap, d_k, d_v, dtype, normalize):
+    """Gated steps from an oracle state (a prefix of 96 gated tokens), with
+    some steps resetting, against the oracle's gated recurrence."""
+    _log(f"decode_gated {fmap} {dtype} normalize={normalize}")
+    B, H, P, T = 3, 5, 96, 8
+    q, k, v = synth.draw_qkv(B, H, P, d_k, d_v, seed=51, dtype=dtype)
+    qs, ks, vs = synth.draw_qkv(B, H, T, d_k, d_v, seed=51, dtype=dtype, stream=1)
+    a0 = synth.draw_gate(B, H, P, seed=51)
+    a = synth.draw_gate(B, H, T, seed=51, lo=0.5, reset_p=0.1, stream=3)
+    S0, z0 = oracle.gated_final_state(k.f64(), v.f64(), a0.astype(np.float64), fmap)
+    S0 = S0.astype(np.float32)
+    z0 = z0.astype(np.float32)
+    y_ref, S_ref, z_ref = oracle.attention_gated_recurrent(
+        qs.f64(), ks.f64(), vs.f64(), a.astype(np.float64), fmap,
+        S0.astype(np.float64), z0.astype(np.float64), normalize=normalize)
+    Sd = torch.from_numpy(S0).to(DEV)
+    zd = torch.from_numpy(z0).to(DEV)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (qs, ks, vs))
+    ad = _gate_dev(a)
+    ys = []
+    for t in range(T):
+        ys.append(ops.decode_step_gated(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(),
+                                        vd[:, :, t].contiguous(), ad[:, :, t].contiguous(),
+                                        Sd, zd, fmap, normalize=normalize))
+    torch.cuda.synchronize()
+    y = ops.to_numpy64(torch.stack(ys, dim=2))
+    assert row_err(y, y_ref) <= TOL[dtype]
+    assert state_err(ops.to_numpy64(Sd), S_ref) <= 1e-4
+    assert state_err(ops.to_numpy64(zd)[..., None], z_ref[..., None]) <= 1e-4
+
+
+def test_gated_prefill_then_decode_matches_one_recurrence():
+    """Gated prefill writes the state, gated decode continues it: the same
+    numbers as one gated recurrence over both parts."""
+    _log("gated prefill -> gated decode")
+    fmap, d_k, d_v = "taylor2sym", 16, 64
+    B, H, P, T = 2, 3, 300, 6
+    q, k, v = synth.draw_qkv(B, H, P + T, d_k, d_v, seed=61, dtype="bf16",
+                             qk_scale=_qk_scale(fmap))
+    a = synth.draw_gate(B, H, P + T, seed=61, lo=0.9, reset_p=0.01)
+    y_ref, S_ref, _ = oracle.attention_gated_recurrent(q.f64(), k.f64(), v.f64(),
+                                                       a.astype(np.float64), fmap)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    ad = _gate_dev(a)
+    y1, (S, z) = ops.prefill_gated(qd[:, :, :P].contiguous(), kd[:, :, :P].contiguous(),
+                                   vd[:, :, :P].contiguous(), ad[:, :, :P].contiguous(),
+                                   fmap, return_state=True)
+    ys = [ops.decode_step_gated(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(),
+                                vd[:, :, t].contiguous(), ad[:, :, t].contiguous(),
+                                S, z, fmap) for t in range(P, P + T)]
+    torch.cuda.synchronize()
+    y = np.concatenate([ops.to_numpy64(y1), ops.to_numpy64(torch.stack(ys, dim=2))], axis=2)
+    assert row_err(y, y_ref) <= TOL["bf16"]
+    assert state_err(ops.to_numpy64(S), S_ref) <= TOL["bf16"]
+
+
 # ------------------------------------------------------ full-size configs --
 def _sampled_rows(n, rng, count=32):
     rows = set([0, n - 1]) | set(rng.integers(0, n, size=count).tolist())
@@ -315,6 +456,36 @@ def test_full_size_prefill(name, heads):
         ref = oracle.attention_rows(q64[b, h], k64[b, h], v64[b, h], fmap, rows)
         assert row_err(y[b, h, rows], ref) <= TOL["bf16"], (b, h)
         S_ref, _ = oracle.final_state(k64[b, h], v64[b, h], fmap)
+        assert state_err(S[b, h][None, None], S_ref[None, None]) <= TOL["bf16"]
+
+
+def test_full_size_gated_prefill():
+    """The bench workload (ELU1, B=8 H=8 N=4096 d=64, bf16) with a in
+    [0.9, 1) and 0.1% resets, default launch: sampled rows and final states
+    of sampled heads against the oracle's gated definition."""
+    _log("full-size gated prefill layer_elu1_bf16")
+    name = "layer_elu1_bf16"
+    cfg = synth.WORKLOADS[name]
+    fmap = cfg["fmap"]
+    B, H, N = cfg["B"], cfg["H"], cfg["N"]
+    q, k, v = synth.workload_inputs(name, seed=0)
+    a = synth.draw_gate(B, H, N, seed=0, lo=0.9, reset_p=0.001)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    y, (S, z) = ops.prefill_gated(qd, kd, vd, _gate_dev(a), fmap, return_state=True)
+    torch.cuda.synchronize()
+    y = ops.to_numpy64(y)
+    S = ops.to_numpy64(S)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(3)
+    q64, k64, v64 = q.f64(), k.f64(), v.f64()
+    a64 = a.astype(np.float64)
+    for _ in range(6):
+        b, h = int(rng.integers(0, B)), int(rng.integers(0, H))
+        rows = _sampled_rows(N, rng)
+        ref = oracle.attention_gated_rows(q64[b, h], k64[b, h], v64[b, h], a64[b, h],
+                                          fmap, rows)
+        assert row_err(y[b, h, rows], ref) <= TOL["bf16"], (b, h)
+        S_ref, _ = oracle.gated_final_state(k64[b, h], v64[b, h], a64[b, h], fmap)
         assert state_err(S[b, h][None, None], S_ref[None, None]) <= TOL["bf16"]
 
 
