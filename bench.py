@@ -12,8 +12,9 @@ per step, all heads).  The same JSON line carries:
                 1024-token prefix, 128 steps; steps/s and its HBM roofline
                 (algorithmic bytes: state read + written, q, k, v, y);
   cpu_baseline  the float64 oracle on the host, on a bounded sample;
-  other_configs the Taylor-2 and 64K-token prefills, and an N sweep (4K to
-                64K tokens) showing time linear in N;
+  other_configs the Taylor-2 and 64K-token prefills, an N sweep (4K to
+                64K tokens) showing time linear in N, and the gated
+                (scalar-decay) prefill on the headline and Taylor shapes;
   roofline.intra_chunk_mfma_probe
                 the MFMA rate of the prefill's within-chunk device code on
                 LDS-resident tiles, looped (liblinattn_probe.so).
@@ -52,9 +53,11 @@ def feature_dim(fmap, d_k):
 
 
 def prefill_bytes(cfg):
+    """q, k, v read and y written once (+ one float32 decay per token and
+    head for the gated form)."""
     es = 2 if cfg["dtype"] == "bf16" else 4
     tok = cfg["B"] * cfg["H"] * cfg["N"]
-    return tok * (2 * cfg["d_k"] + 2 * cfg["d_v"]) * es
+    return tok * ((2 * cfg["d_k"] + 2 * cfg["d_v"]) * es + (4 if cfg.get("gated") else 0))
 
 
 def prefill_flops(cfg):
@@ -70,12 +73,14 @@ def decode_step_bytes(cfg):
     D = feature_dim(cfg["fmap"], cfg["d_k"])
     bh = cfg["B"] * cfg["H"]
     return bh * (2 * D * cfg["d_v"] * 4 + 2 * D * 4
-                 + (2 * cfg["d_k"] + 2 * cfg["d_v"]) * es)
+                 + (2 * cfg["d_k"] + 2 * cfg["d_v"]) * es + (4 if cfg.get("gated") else 0))
 
 
-def time_prefill(args, ops, synth, torch, name=PREFILL, override=None, steps=None):
+def time_prefill(args, ops, synth, torch, name=PREFILL, override=None, steps=None,
+                 gated=False):
     cfg = dict(synth.WORKLOADS[name])
     cfg.update(override or {})
+    cfg["gated"] = gated
     dev = "cuda:0"
     q, k, v = synth.workload_inputs(name, seed=0, **(override or {}))
     base = [ops.to_device(x, dev) for x in (q, k, v)]
@@ -87,19 +92,30 @@ def time_prefill(args, ops, synth, torch, name=PREFILL, override=None, steps=Non
     tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
     nws = ops.workspace_bytes(fmap, tdt, B, H, N, dk, dv, 0)
     stream = ops._stream(base[0])
+    # gated form: a in [0.9, 1) with 0.1% resets
+    gate = (torch.from_numpy(synth.draw_gate(B, H, N, seed=0, lo=0.9, reset_p=0.001)).to(dev)
+            if gated else None)
     sets = []
     for i in range(nsets):
         qd, kd, vd = (t.clone() for t in base) if i else base
         y = torch.empty_like(vd)
         ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
-        sets.append((qd, kd, vd, y, ws))
+        g = (gate.clone() if i else gate) if gated else None
+        sets.append((qd, kd, vd, y, ws, g))
     dcode = 1 if cfg["dtype"] == "bf16" else 0
-    calls = [(ops.MAPS[fmap], dcode, B, H, N, dk, dv, ops._ptr(s[0]), ops._ptr(s[1]),
-              ops._ptr(s[2]), ops._ptr(s[3]), None, None, None, None, 0,
-              ops._ptr(s[4]), nws, stream) for s in sets]
+    if gated:
+        fn = L.linattn_prefill_gated
+        calls = [(ops.MAPS[fmap], dcode, B, H, N, dk, dv, ops._ptr(s[0]), ops._ptr(s[1]),
+                  ops._ptr(s[2]), ops._ptr(s[5]), 1, ops._ptr(s[3]), None, None, None,
+                  None, 0, ops._ptr(s[4]), nws, stream) for s in sets]
+    else:
+        fn = L.linattn_prefill
+        calls = [(ops.MAPS[fmap], dcode, B, H, N, dk, dv, ops._ptr(s[0]), ops._ptr(s[1]),
+                  ops._ptr(s[2]), ops._ptr(s[3]), None, None, None, None, 0,
+                  ops._ptr(s[4]), nws, stream) for s in sets]
 
     def step(i):
-        rc = L.linattn_prefill(*calls[i % nsets])
+        rc = fn(*calls[i % nsets])
         if rc:
             raise RuntimeError(f"linattn_prefill returned {rc}")
 
@@ -127,8 +143,8 @@ def prefill_record(cfg, ms):
             "mfma_frac": prefill_flops(cfg) / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
-def time_decode(args, ops, synth, torch, fmap="taylor2"):
-    cfg = dict(synth.WORKLOADS[DECODE], fmap=fmap)
+def time_decode(args, ops, synth, torch, fmap="taylor2", gated=False):
+    cfg = dict(synth.WORKLOADS[DECODE], fmap=fmap, gated=gated)
     dev = "cuda:0"
     pq, pk, pv, sq, sk, sv = synth.workload_inputs(DECODE, seed=0)
     qd, kd, vd = (ops.to_device(x, dev) for x in (pq, pk, pv))
@@ -139,13 +155,23 @@ def time_decode(args, ops, synth, torch, fmap="taylor2"):
     y = torch.empty((T, cfg["B"], cfg["H"], cfg["d_v"]), dtype=torch.bfloat16, device=dev)
     L = ops.load_library()
     stream = ops._stream(S)
-    calls = [(ops.MAPS[fmap], 1, cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"],
-              ops._ptr(steps[0][t]), ops._ptr(steps[1][t]), ops._ptr(steps[2][t]),
-              ops._ptr(S), ops._ptr(z), ops._ptr(y[t]), stream) for t in range(T)]
+    if gated:
+        gates = torch.from_numpy(synth.draw_gate(T, cfg["B"], cfg["H"], seed=0, lo=0.9,
+                                                 reset_p=0.001)).to(dev)
+        fn = L.linattn_decode_step_gated
+        calls = [(ops.MAPS[fmap], 1, cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"],
+                  ops._ptr(steps[0][t]), ops._ptr(steps[1][t]), ops._ptr(steps[2][t]),
+                  ops._ptr(gates[t]), 1, ops._ptr(S), ops._ptr(z), ops._ptr(y[t]),
+                  stream) for t in range(T)]
+    else:
+        fn = L.linattn_decode_step
+        calls = [(ops.MAPS[fmap], 1, cfg["B"], cfg["H"], cfg["d_k"], cfg["d_v"],
+                  ops._ptr(steps[0][t]), ops._ptr(steps[1][t]), ops._ptr(steps[2][t]),
+                  ops._ptr(S), ops._ptr(z), ops._ptr(y[t]), stream) for t in range(T)]
 
     def generation():
         for c in calls:
-            rc = L.linattn_decode_step(*c)
+            rc = fn(*c)
             if rc:
                 raise RuntimeError(f"linattn_decode_step returned {rc}")
 
@@ -167,7 +193,7 @@ def time_decode(args, ops, synth, torch, fmap="taylor2"):
     with torch.cuda.graph(g):
         cap = ops._stream(S)
         for c in calls:
-            rc = L.linattn_decode_step(*c[:-1], cap)
+            rc = fn(*c[:-1], cap)
             if rc:
                 raise RuntimeError(f"linattn_decode_step returned {rc}")
     g.replay()
@@ -373,6 +399,15 @@ def main():
                                       override={"N": n}, steps=50)
             sweep.append(dict(N=n, **prefill_record(c3, ms3)))
         others["n_sweep_elu1_b1h8_d64_bf16"] = sweep
+        # the gated (scalar-decay) form on the headline and Taylor shapes
+        for name in (PREFILL, "based_taylor2_bf16"):
+            c4, ms4, _ = time_prefill(args, ops, synth, torch, name=name, steps=100,
+                                      gated=True)
+            others["gated_" + name] = dict(
+                prefill_record(c4, ms4),
+                workload=(f"gated prefill (a in [0.9, 1), 0.1% resets) {c4['fmap']} "
+                          f"B={c4['B']} H={c4['H']} N={c4['N']} d_k={c4['d_k']} "
+                          f"d_v={c4['d_v']} {c4['dtype']}"))
     tokens = cfg["B"] * cfg["N"]
     nbytes = prefill_bytes(cfg)
     flops = prefill_flops(cfg)
@@ -444,6 +479,16 @@ def main():
                 "hbm_frac": sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "graph_ms_per_step": sms_graph,
                 "graph_hbm_frac": sbytes / (sms_graph * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            }
+            gcfg, gms, gfinite, gms_graph = time_decode(args, ops, synth, torch,
+                                                        "taylor2", gated=True)
+            gbytes = decode_step_bytes(gcfg)
+            out["decode"]["gated"] = {
+                "workload": "the same decode, gated (a in [0.9, 1), 0.1% resets)",
+                "ms_per_step": gms, "steps_per_s": 1e3 / gms, "finite": gfinite,
+                "algorithmic_bytes": gbytes,
+                "hbm_frac": gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "graph_ms_per_step": gms_graph,
             }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth)

@@ -84,6 +84,16 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r,
   return __builtin_amdgcn_raw_buffer_load_b32(r, byte_offset, 0, 0);
 }
 
+// Lane shift inside a wave through DPP (no LDS round trip): lanes whose
+// source is outside the pattern or in a row excluded by ROWS keep `old`.
+//   row_shr:n (0x110 + n)  lane i of a 16-lane row reads lane i - n of it
+//   row_bcast:15 (0x142)   rows 1, 3 read lane 15 of the row before (ROWS 0xa)
+//   row_bcast:31 (0x143)   rows 2, 3 read lane 31 (ROWS 0xc)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_move(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xf, false);
+}
+
 // elu(x) + 1 without a compare: exp(x) >= 1 + x for every x (convexity),
 // with equality only at 0, and exp(-|x|) <= 1 < 1 + x for x > 0, so
 //   phi(x) = max(1 + x, exp(-|x|))

@@ -257,13 +257,16 @@ struct ChunkTiles {
   // O^T += V'^T A^T for key block jb2, where A^T = scores^T of the block's
   // keys against the wave's 16 queries (operands bq), kept where keep[] is
   // set (the causal mask); TAYLOR2 turns the raw q.k into 1 + s + s^2 / 2.
-  // GATED: each kept score is multiplied by its decay weight dec[] (the
-  // product of the coefficients after the key up to the query).
+  // GATED: each kept score is multiplied by its decay weight, the product
+  // of the coefficients after the key up to the query: 2^(Gq - G[key]) from
+  // the chunk's running log2 sums G (gk = G of keys 32 jb2 + 8 g + 0..7),
+  // or 0 for a key before the query's last reset Lq.
   template <bool GATED = false>
   __device__ static __forceinline__ void within_chunk(const T* sK, const frag (&vf)[NCT - 1],
                                                       const frag (&bq)[SH::NKBS], const bool (&keep)[8],
                                                       const frag& ones, f32x4_t (&O)[NCT], int jb2,
-                                                      int lane, const float* dec = nullptr) {
+                                                      int lane, const float* gk = nullptr,
+                                                      float Gq = 0.0f, int Lq = -1) {
     const int i16 = lane & 15;
     f32x4_t sc[2];
 #pragma unroll
@@ -272,6 +275,16 @@ struct ChunkTiles {
       const int jt = 32 * jb2 + 8 * (i16 >> 2) + 4 * h + (i16 & 3);
 #pragma unroll
       for (int kbs = 0; kbs < SH::NKBS; ++kbs) E::mma(sc[h], k_rows(sK, jt, kbs, lane), bq[kbs]);
+    }
+    float dec[8];
+    if constexpr (GATED) {
+      const float4 g0 = *reinterpret_cast<const float4*>(gk);
+      const float4 g1 = *reinterpret_cast<const float4*>(gk + 4);
+      const float G[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const int key0 = 32 * jb2 + 8 * (lane >> 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        dec[e] = keep[e] && key0 + e >= Lq ? __builtin_amdgcn_exp2f(Gq - G[e]) : 0.0f;
     }
     float f[8];
 #pragma unroll
@@ -336,7 +349,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   constexpr int KT_EL = kNeedKT ? DK * CS : EPU;
   constexpr int V_EL = BF ? C * RTV::STRIDE : DV * CS;
   constexpr int S_EL = OUT ? SH::NCOL * PS : EPU;
-  constexpr int kTileBytes = 2 * (K_EL + KT_EL + V_EL) * (int)sizeof(T) + (GATED ? 2 * C * 8 : 0);
+  constexpr int kTileBytes = 2 * (K_EL + KT_EL + V_EL) * (int)sizeof(T) + (GATED ? 2 * C * 16 : 0);
   constexpr int NSB = kTileBytes + 2 * S_EL * (int)sizeof(T) <= 160 * 1024 ? 2 : 1;
   __shared__ __align__(16) T sK0[K_EL];
   __shared__ __align__(16) T sK1[K_EL];
@@ -348,9 +361,14 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   __shared__ __align__(16) T sS1[NSB == 2 ? S_EL : EPU];
   // Gated form, per LDS copy: sG[b][i] = log2 of the decay accumulated from
   // the chunk's last reset at or before token i (or from the chunk start)
-  // through token i; sL[b][i] = the index of that reset, or -1.
+  // through token i; sL[b][i] = the index of that reset, or -1; sF[b][i] =
+  // the factor of the state carried into the chunk at token i (0 past a
+  // reset); sU[b][i] = the weight of token i at the chunk end (0 across a
+  // reset and past the segment end).
   __shared__ __align__(16) float sG[2][GATED ? C : 1];
   __shared__ __align__(16) int sL[2][GATED ? C : 1];
+  __shared__ __align__(16) float sF[2][GATED ? C : 1];
+  __shared__ __align__(16) float sU[2][GATED ? C : 1];
   auto sK = [&](int b) __attribute__((always_inline)) { return b ? sK1 : sK0; };
   auto sKT = [&](int b) __attribute__((always_inline)) { return b ? sKT1 : sKT0; };
   auto sV = [&](int b) __attribute__((always_inline)) { return b ? sV1 : sV0; };
@@ -527,17 +545,32 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       const bool reset = valid && !(lg >= kResetLog2);
       float G = valid && !reset ? lg : 0.0f;
       int L = reset ? lane : -1;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float Gp = __shfl_up(G, off, 64);
-        const int Lp = __shfl_up(L, off, 64);
-        if (lane >= off && L < 0) {
+      // Inclusive scan of (G, L) under "a later reset wins, else add": steps
+      // of 1, 2, 4, 8 lanes inside each row of 16, then the row totals
+      // through lanes 15 and 31.  A lane without a source receives the
+      // identity (0, -1).
+      auto combine = [&](auto ctrl, auto rows) __attribute__((always_inline)) {
+        constexpr int CTRL = decltype(ctrl)::value, ROWS = decltype(rows)::value;
+        const float Gp = __int_as_float(dpp_move<CTRL, ROWS>(0, __float_as_int(G)));
+        const int Lp = dpp_move<CTRL, ROWS>(-1, L);
+        if (L < 0) {
           G += Gp;
           L = Lp;
         }
-      }
+      };
+      combine(std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xf>{});
+      combine(std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xf>{});
+      combine(std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xf>{});
+      combine(std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{});
+      combine(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{});
+      combine(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{});
+
+      const float Gend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), C - 1));
+      const int Lend = __builtin_amdgcn_readlane(L, C - 1);
       sG[b][lane] = G;
       sL[b][lane] = L;
+      sF[b][lane] = L >= 0 ? 0.0f : __builtin_amdgcn_exp2f(G);
+      sU[b][lane] = valid && lane >= Lend ? __builtin_amdgcn_exp2f(Gend - G) : 0.0f;
     }
   };
 
@@ -776,17 +809,20 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     // Gated form: decays of this chunk.  Query il carries the state from
     // before the chunk with factor fq (0 past a reset); the chunk as a whole
     // scales the carried state by fc.
-    float Gq = 0.0f, Ge = 0.0f, fq = 1.0f, fc = 1.0f;
-    int Lq = -1, Le = -1;
+    float Gq = 0.0f, fq = 1.0f, fc = 1.0f;
+    int Lq = -1;
     if constexpr (GATED) {
-      Ge = sG[b][C - 1];
-      Le = sL[b][C - 1];
-      fc = Le >= 0 ? 0.0f : __builtin_amdgcn_exp2f(Ge);
+      // chunk-end values are the same for every lane: keep them scalar
+      fc = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                         __builtin_bit_cast(int, sF[b][C - 1])));
       if constexpr (OUT) {
         Gq = sG[b][il];
         Lq = sL[b][il];
-        fq = Lq >= 0 ? 0.0f : __builtin_amdgcn_exp2f(Gq);
+        fq = sF[b][il];
       } else {
+        const float Ge = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                       __builtin_bit_cast(int, sG[b][C - 1])));
+        const int Le = __builtin_amdgcn_readfirstlane(sL[b][C - 1]);
         seg_log = Le >= 0 ? -__builtin_inff() : seg_log + Ge;
       }
     }
@@ -856,21 +892,15 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 #pragma unroll
       for (int ct = 0; ct < NCT - 1; ++ct) vf[ct] = v_frag(b, jb2, ct);
 
-      // Gated form: weight of key 32 jb2 + 8 g + e at query il (dec) and at
-      // the chunk end (u); zero across a reset, and u is zero for tokens past
-      // the segment end so that they add nothing to the state.
-      float dec[8], u[8];
+      // Gated form: weight u of key 32 jb2 + 8 g + e at the chunk end (zero
+      // across a reset, and past the segment end so that those tokens add
+      // nothing to the state).
+      float u[8];
       if constexpr (GATED) {
-        const float4 g0 = *reinterpret_cast<const float4*>(&sG[b][32 * jb2 + 8 * g]);
-        const float4 g1 = *reinterpret_cast<const float4*>(&sG[b][32 * jb2 + 8 * g + 4]);
-        const float Gk[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = 32 * jb2 + 8 * g + e;
-          if constexpr (OUT)
-            dec[e] = keep[jb2][e] && key >= Lq ? __builtin_amdgcn_exp2f(Gq - Gk[e]) : 0.0f;
-          u[e] = key >= Le && cb + key < ntok ? __builtin_amdgcn_exp2f(Ge - Gk[e]) : 0.0f;
-        }
+        const float4 u0 = *reinterpret_cast<const float4*>(&sU[b][32 * jb2 + 8 * g]);
+        const float4 u1 = *reinterpret_cast<const float4*>(&sU[b][32 * jb2 + 8 * g + 4]);
+        u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w;
+        u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
       }
 
       if constexpr (OUT) {
@@ -881,7 +911,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
         for (int kbs = 0; kbs < SH::NKBS; ++kbs) {
           if constexpr (MAP == MAP_ELU1) bq[kbs] = q_frag(b, kbs); else bq[kbs] = qraw;
         }
-        CT::template within_chunk<GATED>(sK(b), vf, bq, keep[jb2], ones, O, jb2, lane, dec);
+        CT::template within_chunk<GATED>(sK(b), vf, bq, keep[jb2], ones, O, jb2, lane,
+                                         GATED ? &sG[b][32 * jb2 + 8 * g] : nullptr, Gq, Lq);
       }
 
       // state update: S' += phi(K)^T V' for this wave's row tiles
