@@ -25,5 +25,9 @@ from .linattn_oracle import (  # noqa: F401
     phi_elu1,
     phi_taylor2,
     phi_taylor2_sym,
+    swa_attention,
+    swa_cache_after_prefill,
+    swa_decode_step,
+    swa_rows,
     sym_pairs,
 )

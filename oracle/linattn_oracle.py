@@ -14,6 +14,8 @@ Sources (page titles as printed; section in brackets):
         the recurrent state equations, the Taylor kernel identity) and Knowl 5
         (prefill writes final states; generation updates the state, then reads
         it).
+        Knowl 4 (sliding-window exact attention: query i sees keys
+        max(1, i-w+1) .. i, a w-token key-value cache in generation).
   [HN]  the discussion page of "Transformers are RNNs" (hackerpapers),
         section "In the conversation": one comment writes the gated linear
         recurrences as a state decayed by a forget factor plus a gated outer
@@ -48,6 +50,13 @@ Readings taken where the pages are silent (each is listed in the design doc):
     j = i).  The output is either the [SLA] Knowl 3 ratio of the decayed sums
     (normalize=True) or the comment's unnormalised read phi(q_t) S_t
     (normalize=False).
+  * Sliding-window attention ([SLA] Knowl 4) is softmax attention with the
+    score scale * q.k; the pages name it exact softmax attention and the
+    page on the Taylor approximation calls the target "standard scaled
+    dot-product attention", so the default scale is 1/sqrt(d) (the kernels
+    take it as an argument).  The window counts the query's own key, so
+    w = 1 returns v_i.  The generation cache is a ring of w slots: token t
+    lives in slot t mod w.
 
 Parity pins (all in tests/test_oracle_pins.py): exact rational brute force,
 quadratic == recurrent, Taylor identity and its exp limit, torch's elu,
@@ -370,6 +379,79 @@ def attention_gated_rows(q, k, v, a, fmap: str, rows, normalize=True) -> np.ndar
         if normalize:
             out[r] /= w.sum()
     return out
+
+
+# --------------------------------------------------------------------------
+# Sliding-window softmax attention ([SLA] Knowl 4)
+# --------------------------------------------------------------------------
+def swa_attention(q, k, v, window: int, scale: float) -> np.ndarray:
+    """y_i = sum_j p_ij v_j, p_i = softmax over j in [i - w + 1, i] (0-based,
+    clipped at 0) of scale * q_i . k_j.
+
+    q, k: [..., N, d_k]; v: [..., N, d_v].  Dense band mask: small N only
+    (swa_rows evaluates single rows at any N).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    n = q.shape[-2]
+    s = scale * (q @ np.swapaxes(k, -1, -2))
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    band = (j <= i) & (j > i - window)
+    s = np.where(band, s, -np.inf)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    return p @ v
+
+
+def swa_rows(q, k, v, window: int, scale: float, rows) -> np.ndarray:
+    """The same definition at the (0-based) positions `rows` of ONE sequence
+    and head (q, k: [N, d_k], v: [N, d_v]); O(w d) per row, any N."""
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    out = np.empty((len(rows), v.shape[-1]), dtype=np.float64)
+    for r, t in enumerate(rows):
+        lo = max(0, t - window + 1)
+        s = scale * (k[lo:t + 1] @ q[t])
+        p = np.exp(s - s.max())
+        out[r] = (p / p.sum()) @ v[lo:t + 1]
+    return out
+
+
+def swa_cache_after_prefill(k, v, window: int):
+    """The w-slot key/value cache after N tokens: token t in slot t mod w for
+    the last min(N, w) tokens; slots never written hold zeros.
+    k: [..., N, d_k]; v: [..., N, d_v] -> ([..., w, d_k], [..., w, d_v])."""
+    k = _f64(k)
+    v = _f64(v)
+    n = k.shape[-2]
+    kc = np.zeros(k.shape[:-2] + (window, k.shape[-1]))
+    vc = np.zeros(v.shape[:-2] + (window, v.shape[-1]))
+    for t in range(max(0, n - window), n):
+        kc[..., t % window, :] = k[..., t, :]
+        vc[..., t % window, :] = v[..., t, :]
+    return kc, vc
+
+
+def swa_decode_step(q, k, v, k_cache, v_cache, pos: int, window: int, scale: float):
+    """One generation step at 0-based position `pos`: write (k, v) into slot
+    pos mod w, then attend over the min(pos + 1, w) most recent tokens.
+    q, k: [..., d_k]; v: [..., d_v]; caches [..., w, d].  Returns
+    (y, k_cache', v_cache'); the inputs are not modified."""
+    kc = _f64(k_cache).copy()
+    vc = _f64(v_cache).copy()
+    kc[..., pos % window, :] = _f64(k)
+    vc[..., pos % window, :] = _f64(v)
+    valid = [t % window for t in range(max(0, pos - window + 1), pos + 1)]
+    s = scale * np.einsum("...d,...jd->...j", _f64(q), kc[..., valid, :])
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    y = np.einsum("...j,...jd->...d", p, vc[..., valid, :])
+    return y, kc, vc
 
 
 def kernel_value(q, k, fmap: str) -> np.ndarray:

@@ -26,6 +26,12 @@ recall-throughput tradeoff" = SLA; "Transformers are RNNs ..." = TR):
                    for a constant decay, a reset (a_t = 0) cutting the past
                    off, a = 0 and a = 1 as closed forms, continuation through
                    a state, and the final state summed three ways
+  swa_*            sliding-window softmax attention (SLA Knowl 4): torch's
+                   scaled_dot_product_attention with a causal or band mask
+                   (a library routine), w = 1, a two-key closed form through
+                   the logistic function, constant keys as a moving average
+                   (numpy's convolve), locality, rows, and the ring cache
+                   with decode steps continuing a prefill
   closed forms     first token, constant key, zero Taylor query, constant v,
                    linearity in v, convex hull, positivity, final state,
                    decode continuation, sampled rows, hand-worked golden file
@@ -587,6 +593,101 @@ def pin_gated_continuation_and_state(o):
             assert _rel(got, want) < 1e-12
 
 
+# ------------------------------------------------------ sliding window ----
+def pin_swa_matches_torch_sdpa(o):
+    """Band-masked softmax attention equals torch's scaled_dot_product_attention
+    with the same boolean band mask; w >= N is its causal mode."""
+    import torch
+    r = _rng(31)
+    q = r.standard_normal((2, 3, 70, 8))
+    k = r.standard_normal((2, 3, 70, 8))
+    v = r.standard_normal((2, 3, 70, 5))
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    for w in (1, 3, 16, 40, 70, 100):
+        i = torch.arange(70)[:, None]
+        j = torch.arange(70)[None, :]
+        band = (j <= i) & (j > i - w)
+        for scale in (8 ** -0.5, 0.3):
+            want = torch.nn.functional.scaled_dot_product_attention(
+                tq, tk, tv, attn_mask=band, scale=scale).numpy()
+            assert _rel(o.swa_attention(q, k, v, w, scale), want) < 1e-12, (w, scale)
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True).numpy()
+    assert _rel(o.swa_attention(q, k, v, 70, 8 ** -0.5), want) < 1e-12
+
+
+def pin_swa_closed_forms(o):
+    """w = 1 returns v.  w = 2: y_i = v_i + sigma(a - b) (v_{i-1} - v_i) with
+    a, b the scaled scores of keys i-1 and i (logistic written with math.exp).
+    Constant keys: equal weights, so y_i is the mean of the last
+    min(i + 1, w) values (numpy's convolve)."""
+    r = _rng(32)
+    q = r.standard_normal((30, 4))
+    k = r.standard_normal((30, 4))
+    v = r.standard_normal((30, 3))
+    assert _rel(o.swa_attention(q, k, v, 1, 0.5), v) < 1e-15
+    y2 = o.swa_attention(q, k, v, 2, 0.5)
+    for i in range(1, 30):
+        a = 0.5 * float(q[i] @ k[i - 1])
+        b = 0.5 * float(q[i] @ k[i])
+        sig = 1.0 / (1.0 + math.exp(-(a - b)))
+        assert _rel(y2[i], v[i] + sig * (v[i - 1] - v[i])) < 1e-13
+    assert _rel(y2[0], v[0]) < 1e-15
+    kc = np.tile(r.standard_normal((1, 4)), (30, 1))
+    for w in (1, 4, 7, 30):
+        y = o.swa_attention(q, kc, v, w, 0.5)
+        counts = np.convolve(np.ones(30), np.ones(w))[:30]
+        means = np.stack([np.convolve(v[:, c], np.ones(w))[:30] for c in range(3)], -1)
+        assert _rel(y, means / counts[:, None]) < 1e-12, w
+
+
+def pin_swa_locality_and_rows(o):
+    """Changing tokens outside row i's window leaves y_i unchanged; single
+    rows agree with the dense form."""
+    r = _rng(33)
+    q = r.standard_normal((60, 6))
+    k = r.standard_normal((60, 6))
+    v = r.standard_normal((60, 4))
+    w = 9
+    y = o.swa_attention(q, k, v, w, 0.4)
+    k2, v2 = k.copy(), v.copy()
+    k2[:30] = r.standard_normal((30, 6))   # before row 40's window [32, 40]
+    v2[:30] = r.standard_normal((30, 4))
+    k2[41:] = r.standard_normal((19, 6))   # after row 40
+    v2[41:] = r.standard_normal((19, 4))
+    y2 = o.swa_attention(q, k2, v2, w, 0.4)
+    assert _rel(y2[38:41], y[38:41]) < 1e-14
+    assert _rel(y2[:30], y[:30]) > 1e-3    # and the change is visible elsewhere
+    rows = [0, 1, 8, 9, 10, 59]
+    assert _rel(o.swa_rows(q, k, v, w, 0.4, rows), y[rows]) < 1e-13
+
+
+def pin_swa_decode_continues_prefill(o):
+    """Cache from a prefill of P tokens, then T decode steps, equals the dense
+    form over all P + T tokens; the cache built step by step equals the one
+    from the prefill."""
+    r = _rng(34)
+    for w, P in ((5, 12), (16, 3), (7, 7)):
+        T = 11
+        q = r.standard_normal((2, P + T, 4))
+        k = r.standard_normal((2, P + T, 4))
+        v = r.standard_normal((2, P + T, 3))
+        want = o.swa_attention(q, k, v, w, 0.7)
+        kc, vc = o.swa_cache_after_prefill(k[:, :P], v[:, :P], w)
+        for t in range(P, P + T):
+            kc0 = kc.copy()
+            y, kc, vc = o.swa_decode_step(q[:, t], k[:, t], v[:, t], kc, vc, t, w, 0.7)
+            assert _rel(y, want[:, t]) < 1e-12, (w, P, t)
+        kc2, vc2 = o.swa_cache_after_prefill(k, v, w)
+        assert _rel(kc, kc2) < 1e-15 and _rel(vc, vc2) < 1e-15
+        # from an empty cache, step by step from token 0
+        kc = np.zeros((2, w, 4))
+        vc = np.zeros((2, w, 3))
+        for t in range(P + T):
+            y, kc, vc = o.swa_decode_step(q[:, t], k[:, t], v[:, t], kc, vc, t, w, 0.7)
+            assert _rel(y, want[:, t]) < 1e-12
+        assert np.array_equal(kc0.shape, kc.shape)
+
+
 PINS = [
     pin_exact_elu1,
     pin_exact_taylor2,
@@ -614,4 +715,8 @@ PINS = [
     pin_gated_zero_and_one,
     pin_gated_reset_cuts_the_past,
     pin_gated_continuation_and_state,
+    pin_swa_matches_torch_sdpa,
+    pin_swa_closed_forms,
+    pin_swa_locality_and_rows,
+    pin_swa_decode_continues_prefill,
 ]

@@ -237,6 +237,42 @@ def _m_gated_normalize_ignored(o):
     o.attention_gated_quadratic = lambda q, k, v, a, fmap, normalize=True: f(q, k, v, a, fmap, True)
 
 
+def _swa_band(lo_fn):
+    def swa(q, k, v, window, scale):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        n = q.shape[-2]
+        s = scale * (q @ np.swapaxes(k, -1, -2))
+        i = np.arange(n)[:, None]
+        j = np.arange(n)[None, :]
+        s = np.where(lo_fn(i, j, window), s, -np.inf)
+        p = np.exp(s - s.max(axis=-1, keepdims=True))
+        return (p / p.sum(axis=-1, keepdims=True)) @ v
+    return swa
+
+
+def _m_swa_window_one_wider(o):
+    o.swa_attention = _swa_band(lambda i, j, w: (j <= i) & (j >= i - w))
+
+
+def _m_swa_not_causal(o):
+    o.swa_attention = _swa_band(lambda i, j, w: np.abs(i - j) < w)
+
+
+def _m_swa_no_scale(o):
+    f = o.swa_attention
+    o.swa_attention = lambda q, k, v, window, scale: f(q, k, v, window, 1.0)
+
+
+def _m_swa_decode_wrong_slot(o):
+    f = o.swa_decode_step
+    o.swa_decode_step = lambda q, k, v, kc, vc, pos, w, s: f(q, k, v, kc, vc, pos + 1, w, s)
+
+
+def _m_swa_rows_window_short(o):
+    f = o.swa_rows
+    o.swa_rows = lambda q, k, v, window, scale, rows: f(q, k, v, max(1, window - 1), scale, rows)
+
+
 MUTANTS = [
     _m_elu_no_exp, _m_elu_plain_exp, _m_elu_missing_plus_one,
     _m_taylor_no_sqrt2, _m_taylor_no_constant, _m_taylor_wrong_layout,
@@ -245,6 +281,8 @@ MUTANTS = [
     _m_sym_square_unscaled, _m_sym_pair_scaled, _m_sym_pair_doubled, _m_sym_lower_order,
     _m_gated_decay_after_add, _m_gated_z_not_decayed, _m_gated_matrix_own_factor,
     _m_gated_suffix_own_factor, _m_gated_normalize_ignored,
+    _m_swa_window_one_wider, _m_swa_not_causal, _m_swa_no_scale, _m_swa_decode_wrong_slot,
+    _m_swa_rows_window_short,
 ]
 
 
