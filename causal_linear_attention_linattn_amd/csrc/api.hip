@@ -308,6 +308,37 @@ linattn_status_t decode_common(int map, int dtype, int64_t B, int64_t H,
   return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
+bool swa_dim_ok(int64_t d) { return d == 32 || d == 64 || d == 128; }
+
+hipError_t dispatch_swa_prefill(int dtype, int64_t d, const void* q, const void* k,
+                                const void* v, void* y, void* kc, void* vc, int64_t BH,
+                                int64_t N, int64_t window, float scale, hipStream_t st) {
+#define X(D)                                                                          \
+  if (d == D)                                                                         \
+    return dtype == LINATTN_DTYPE_F32                                                 \
+               ? launch_swa_prefill<float, D>(q, k, v, y, kc, vc, BH, N, window, scale, st) \
+               : launch_swa_prefill<bf16_t, D>(q, k, v, y, kc, vc, BH, N, window, scale, st);
+  X(32) X(64) X(128)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_swa_decode(int dtype, int64_t d, const void* q, const void* k,
+                               const void* v, const int64_t* pos, void* kc, void* vc,
+                               void* y, int64_t B, int64_t H, int64_t window, float scale,
+                               hipStream_t st) {
+#define X(D)                                                                              \
+  if (d == D)                                                                             \
+    return dtype == LINATTN_DTYPE_F32                                                     \
+               ? launch_swa_decode<float, D>(q, k, v, pos, kc, vc, y, B, H, window, scale, st) \
+               : launch_swa_decode<bf16_t, D>(q, k, v, pos, kc, vc, y, B, H, window, scale, st);
+  X(32) X(64) X(128)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+bool finite(float x) { return x == x && x - x == 0.0f; }
+
 }  // namespace
 
 extern "C" {
@@ -423,6 +454,81 @@ linattn_status_t linattn_decode_step_gated(int map, int dtype, int64_t B, int64_
                                            float* z, void* y, void* stream) {
   return decode_common(map, dtype, B, H, d_k, d_v, q, k, v, true, gate, normalize, S,
                        z, y, stream);
+}
+
+linattn_status_t linattn_swa_prefill(int dtype, int64_t B, int64_t H, int64_t N,
+                                     int64_t d, int64_t window, float scale,
+                                     const void* q, const void* k, const void* v,
+                                     void* y, void* k_cache, void* v_cache,
+                                     void* stream) {
+  if (!valid_dtype(dtype) || B <= 0 || H <= 0 || N <= 0 || d <= 0 || window <= 0 ||
+      !finite(scale))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!swa_dim_ok(d)) return LINATTN_ERR_UNSUPPORTED;
+  if (B > kMaxElems / H) return LINATTN_ERR_INVALID_ARGUMENT;
+  const int64_t BH = B * H;
+  const size_t es = elem_size(dtype);
+  // one sequence's rows must fit a buffer descriptor; the grid must fit
+  if (N > kMaxSegBytes / (d * (int64_t)es)) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (BH > INT_MAX / ((N + 63) / 64)) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (q == nullptr || k == nullptr || v == nullptr || y == nullptr)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if ((k_cache == nullptr) != (v_cache == nullptr)) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
+      (k_cache && (!aligned16(k_cache) || !aligned16(v_cache))))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (k_cache && BH > kMaxElems / (window * d)) return LINATTN_ERR_INVALID_ARGUMENT;
+  const Range rq = rng(q, BH * N * d, es), rk = rng(k, BH * N * d, es);
+  const Range rv = rng(v, BH * N * d, es), ry = rng(y, BH * N * d, es);
+  const int64_t ncache = k_cache ? BH * window * d : 0;
+  const Range rkc = rng(k_cache, ncache, es), rvc = rng(v_cache, ncache, es);
+  const Range outs[3] = {ry, rkc, rvc};
+  const Range ins[3] = {rq, rk, rv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(outs[i], ins[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = dispatch_swa_prefill(dtype, d, q, k, v, y, k_cache, v_cache, BH, N,
+                                            window, scale,
+                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
+linattn_status_t linattn_swa_decode_step(int dtype, int64_t B, int64_t H, int64_t d,
+                                         int64_t window, float scale, const void* q,
+                                         const void* k, const void* v, const int64_t* pos,
+                                         void* k_cache, void* v_cache, void* y,
+                                         void* stream) {
+  if (!valid_dtype(dtype) || B <= 0 || H <= 0 || d <= 0 || window <= 0 || !finite(scale))
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!swa_dim_ok(d) || window > kSwaMaxWindow) return LINATTN_ERR_UNSUPPORTED;
+  if (B > kMaxElems / H) return LINATTN_ERR_INVALID_ARGUMENT;
+  const int64_t BH = B * H;
+  if (BH > INT_MAX || BH > kMaxElems / (window * d)) return LINATTN_ERR_INVALID_ARGUMENT;
+  if (q == nullptr || k == nullptr || v == nullptr || pos == nullptr || k_cache == nullptr ||
+      v_cache == nullptr || y == nullptr)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(y) ||
+      !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)pos & 7u) != 0)
+    return LINATTN_ERR_INVALID_ARGUMENT;
+  const size_t es = elem_size(dtype);
+  const Range rq = rng(q, BH * d, es), rk = rng(k, BH * d, es), rv = rng(v, BH * d, es);
+  const Range rp = rng(pos, B, 8), ry = rng(y, BH * d, es);
+  const Range rkc = rng(k_cache, BH * window * d, es), rvc = rng(v_cache, BH * window * d, es);
+  const Range outs[3] = {ry, rkc, rvc};
+  const Range ins[4] = {rq, rk, rv, rp};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlap(outs[i], ins[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return LINATTN_ERR_INVALID_ARGUMENT;
+  }
+  const hipError_t e = dispatch_swa_decode(dtype, d, q, k, v, pos, k_cache, v_cache, y, B, H,
+                                           window, scale,
+                                           reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
 }  // extern "C"

@@ -78,6 +78,22 @@ hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* gate, int normalize, float* S, float* z,
                          void* y, int64_t BH, hipStream_t st);
 
+// Sliding-window attention (d_k = d_v = D).  The prefill writes the ring
+// cache only if kc is non-null.  The generation step holds one float per
+// filled slot in LDS, which bounds its window.
+constexpr int kSwaMaxWindow = 4096;
+
+template <typename T, int D>
+hipError_t launch_swa_prefill(const void* q, const void* k, const void* v, void* y,
+                              void* kc, void* vc, int64_t BH, int64_t N,
+                              int64_t window, float scale, hipStream_t st);
+
+template <typename T, int D>
+hipError_t launch_swa_decode(const void* q, const void* k, const void* v,
+                             const int64_t* pos, void* kc, void* vc, void* y,
+                             int64_t B, int64_t H, int64_t window, float scale,
+                             hipStream_t st);
+
 template <int MAP, typename T>
 hipError_t launch_feature_map(const void* x, int64_t rows, int d_k,
                               float* phi, hipStream_t st);

@@ -11,6 +11,8 @@ Entry points (same names as the C ABI in include/linattn.h):
     decode_step(q, k, v, S, z, fmap)          -> y; S, z updated in place
     prefill_gated(q, k, v, gate, fmap, ...)   -> y (and the final state)
     decode_step_gated(q, k, v, gate, S, z, fmap) -> y; S, z updated in place
+    swa_prefill(q, k, v, window, ...)          -> y (and the ring cache)
+    swa_decode_step(q, k, v, pos, kc, vc, window) -> y; caches updated
 """
 from __future__ import annotations
 
@@ -74,6 +76,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.linattn_decode_step_gated.argtypes = [i32, i32, i64, i64, i64, i64, vp, vp, vp,
                                             fp, i32, fp, fp, vp, vp]
     L.linattn_decode_step_gated.restype = i32
+    L.linattn_swa_prefill.argtypes = [i32, i64, i64, i64, i64, i64, ctypes.c_float, vp, vp,
+                                      vp, vp, vp, vp, vp]
+    L.linattn_swa_prefill.restype = i32
+    L.linattn_swa_decode_step.argtypes = [i32, i64, i64, i64, i64, ctypes.c_float, vp, vp,
+                                          vp, vp, vp, vp, vp, vp]
+    L.linattn_swa_decode_step.restype = i32
     _lib = L
     return L
 
@@ -247,6 +255,50 @@ def _decode(q, k, v, gate, normalize, S, z, fmap, out):
                                            _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                                            1 if normalize else 0, _ptr(S), _ptr(z),
                                            _ptr(y), _stream(q)))
+    return y
+
+
+def swa_prefill(q, k, v, window: int, *, scale=None, return_cache=False, out=None):
+    """Sliding-window softmax attention over [B, H, N, d] inputs.
+
+    scale defaults to 1/sqrt(d).  return_cache: also return the ring caches
+    (k_cache, v_cache) [B, H, window, d] for swa_decode_step."""
+    L = load_library()
+    _need_cuda(q, k, v)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("expected q, k, v [B,H,N,d] of one shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    B, H, N, d = q.shape
+    sc = float(d) ** -0.5 if scale is None else float(scale)
+    y = out if out is not None else torch.empty_like(v)
+    _need_cuda(y)
+    kc = vc = None
+    if return_cache:
+        kc = torch.empty((B, H, window, d), dtype=q.dtype, device=q.device)
+        vc = torch.empty_like(kc)
+    _check(L.linattn_swa_prefill(_dtype_id(q), B, H, N, d, window, sc, _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(y), _ptr(kc), _ptr(vc), _stream(q)))
+    if return_cache:
+        return y, (kc, vc)
+    return y
+
+
+def swa_decode_step(q, k, v, pos, k_cache, v_cache, window: int, *, scale=None, out=None):
+    """One sliding-window generation step; q, k, v [B,H,d]; pos int64 [B]
+    (0-based position of this token per sequence); caches updated in place."""
+    L = load_library()
+    _need_cuda(q, k, v, pos, k_cache, v_cache)
+    B, H, d = q.shape
+    if pos.dtype != torch.int64 or tuple(pos.shape) != (B,):
+        raise ValueError("pos must be int64 [B]")
+    if tuple(k_cache.shape) != (B, H, window, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, H, window, d]")
+    sc = float(d) ** -0.5 if scale is None else float(scale)
+    y = out if out is not None else torch.empty_like(v)
+    _check(L.linattn_swa_decode_step(_dtype_id(q), B, H, d, window, sc, _ptr(q), _ptr(k),
+                                     _ptr(v), _ptr(pos), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(y), _stream(q)))
     return y
 
 

@@ -214,6 +214,52 @@ linattn_status_t linattn_decode_step_gated(int map, int dtype, int64_t B, int64_
                                            const float* gate, int normalize, float* S,
                                            float* z, void* y, void* stream);
 
+/*
+ * Sliding-window softmax attention, prefill ("Simple linear attention ...",
+ * Knowl 4: query i attends only to keys max(1, i-w+1) .. i; the BASED
+ * model pairs it with the Taylor linear attention).  For every position i
+ * (0-based) of every sequence and head:
+ *     p_ij = softmax over j in [max(0, i-w+1), i] of scale * q_i . k_j,
+ *     y_i  = sum_j p_ij v_j.
+ *   q, k, v, y  [B, H, N, d] of `dtype` (d_k = d_v = d); d in {32, 64, 128}.
+ *   window      w >= 1 (w >= N is causal softmax attention).
+ *   scale       any finite float; 1/sqrt(d) is the usual choice.
+ *   k_cache, v_cache  [B, H, w, d] of `dtype`, or both NULL: when given,
+ *               they receive the ring cache that linattn_swa_decode_step
+ *               continues from -- token t (t >= N - w) in slot t mod w,
+ *               zeros in slots no token has reached (N < w).
+ * Scores, the running maximum and the sums are float32; bf16 inputs feed
+ * bf16 MFMA products, and the softmax weights enter the value product as
+ * bf16.  y is rounded to dtype.  One sequence's rows must stay below 2 GiB.
+ * No workspace; outputs must not overlap inputs or each other.
+ */
+linattn_status_t linattn_swa_prefill(int dtype, int64_t B, int64_t H, int64_t N,
+                                     int64_t d, int64_t window, float scale,
+                                     const void* q, const void* k, const void* v,
+                                     void* y, void* k_cache, void* v_cache,
+                                     void* stream);
+
+/*
+ * Sliding-window generation step (same page, Knowl 4: a w-token key-value
+ * cache; Knowl 5: the generation kernel fuses the query-key product, the
+ * softmax and the value product).  For every sequence b and head h at the
+ * 0-based position p = pos[b]: write k, v into slot p mod w of the caches,
+ * then attend over the min(p + 1, w) tokens p - w + 1 .. p held there.
+ *   q, k, v, y  [B, H, d] of `dtype`;  d in {32, 64, 128}.
+ *   pos         [B] int64 device array, 8-byte aligned, read only (the
+ *               caller advances it); a negative entry makes that sequence's
+ *               y NaN and leaves its cache unchanged.
+ *   k_cache, v_cache  [B, H, w, d] of `dtype`, updated in place; slots not
+ *               yet reached are never read.
+ *   window      1 <= w <= 4096 (else LINATTN_ERR_UNSUPPORTED).
+ * All arithmetic is float32; y is rounded to dtype.
+ */
+linattn_status_t linattn_swa_decode_step(int dtype, int64_t B, int64_t H, int64_t d,
+                                         int64_t window, float scale, const void* q,
+                                         const void* k, const void* v, const int64_t* pos,
+                                         void* k_cache, void* v_cache, void* y,
+                                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -420,6 +420,95 @@ def test_gated_prefill_then_decode_matches_one_recurrence():
     assert state_err(ops.to_numpy64(S), S_ref) <= TOL["bf16"]
 
 
+# ---------------------------------------------------- sliding window ------
+def _stored_f64(x):
+    return x.f64()
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,w", [(1, 1), (63, 64), (65, 16), (200, 64), (517, 100),
+                                 (300, 1000), (130, 1)])
+def test_swa_prefill_small(d, dtype, N, w):
+    """Sliding-window prefill against the oracle's band-masked softmax, and
+    the ring cache it leaves (bit-exact copies of k, v rows)."""
+    _log(f"swa_prefill d={d} {dtype} N={N} w={w}")
+    q, k, v = synth.draw_qkv(2, 3, N, d, d, seed=N + w, dtype=dtype)
+    scale = d ** -0.5
+    y_ref = oracle.swa_attention(q.f64(), k.f64(), v.f64(), w, scale)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    y, (kc, vc) = ops.swa_prefill(qd, kd, vd, w, return_cache=True)
+    torch.cuda.synchronize()
+    assert row_err(ops.to_numpy64(y), y_ref) <= TOL[dtype]
+    kc_ref, vc_ref = oracle.swa_cache_after_prefill(k.f64(), v.f64(), w)
+    assert np.array_equal(ops.to_numpy64(kc), kc_ref)
+    assert np.array_equal(ops.to_numpy64(vc), vc_ref)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("w,P", [(64, 100), (16, 5), (100, 40)])
+def test_swa_decode_continues_prefill(d, dtype, w, P):
+    """Prefill P tokens (writing the caches), then 12 decode steps: every
+    step's output equals the oracle's dense form over all P + 12 tokens."""
+    _log(f"swa_decode d={d} {dtype} w={w} P={P}")
+    B, H, T = 2, 3, 12
+    q, k, v = synth.draw_qkv(B, H, P + T, d, d, seed=7 + w, dtype=dtype)
+    scale = 0.7 * d ** -0.5
+    y_ref = oracle.swa_attention(q.f64(), k.f64(), v.f64(), w, scale)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    sl = lambda x: x[:, :, :P].contiguous()
+    _, (kc, vc) = ops.swa_prefill(sl(qd), sl(kd), sl(vd), w, scale=scale, return_cache=True)
+    pos = torch.full((B,), P, dtype=torch.int64, device=DEV)
+    ys = []
+    for t in range(P, P + T):
+        ys.append(ops.swa_decode_step(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(),
+                                      vd[:, :, t].contiguous(), pos, kc, vc, w, scale=scale))
+        pos += 1
+    torch.cuda.synchronize()
+    y = ops.to_numpy64(torch.stack(ys, dim=2))
+    assert row_err(y, y_ref[:, :, P:]) <= TOL[dtype]
+    kc_ref, vc_ref = oracle.swa_cache_after_prefill(k.f64(), v.f64(), w)
+    assert np.array_equal(ops.to_numpy64(kc), kc_ref)
+    assert np.array_equal(ops.to_numpy64(vc), vc_ref)
+
+
+def test_swa_decode_positions_per_sequence():
+    """Sequences at different positions in one step (one from an empty cache
+    at 0, one deep in the ring), and a negative position: NaN output and an
+    untouched cache for that sequence only."""
+    _log("swa_decode per-sequence positions")
+    d, w, T = 64, 32, 40
+    q, k, v = synth.draw_qkv(3, 2, 200, d, d, seed=9, dtype="f32")
+    scale = d ** -0.5
+    starts = [0, 150, 0]
+    kc = np.zeros((3, 2, w, d), dtype=np.float32)
+    vc = np.zeros((3, 2, w, d), dtype=np.float32)
+    k64, v64 = k.f64(), v.f64()
+    kc1, vc1 = oracle.swa_cache_after_prefill(k64[1:2, :, :150], v64[1:2, :, :150], w)
+    kc[1:2], vc[1:2] = kc1, vc1
+    kcd = torch.from_numpy(kc).to(DEV)
+    vcd = torch.from_numpy(vc).to(DEV)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    pos = torch.tensor([0, 150, -1], dtype=torch.int64, device=DEV)
+    ys = []
+    for t in range(T):
+        idx = torch.tensor([starts[0] + t, starts[1] + t, 0], device=DEV)
+        pick = lambda x: torch.stack([x[b, :, idx[b]] for b in range(3)]).contiguous()
+        ys.append(ops.swa_decode_step(pick(qd), pick(kd), pick(vd), pos, kcd, vcd, w))
+        pos[:2] += 1
+    torch.cuda.synchronize()
+    y = ops.to_numpy64(torch.stack(ys, dim=2))       # [3, 2, T, d]
+    q64 = q.f64()
+    for b in range(2):
+        for h in range(2):
+            rows = list(range(starts[b], starts[b] + T))
+            ref = oracle.swa_rows(q64[b, h], k64[b, h], v64[b, h], w, scale, rows)
+            assert row_err(y[b, h], ref) <= TOL["f32"], (b, h)
+    assert np.all(np.isnan(y[2]))
+    assert np.array_equal(ops.to_numpy64(kcd[2]), np.zeros((2, w, d)))
+
+
 # ------------------------------------------------------ full-size configs --
 def _sampled_rows(n, rng, count=32):
     rows = set([0, n - 1]) | set(rng.integers(0, n, size=count).tolist())
@@ -487,6 +576,39 @@ def test_full_size_gated_prefill():
         assert row_err(y[b, h, rows], ref) <= TOL["bf16"], (b, h)
         S_ref, _ = oracle.gated_final_state(k64[b, h], v64[b, h], a64[b, h], fmap)
         assert state_err(S[b, h][None, None], S_ref[None, None]) <= TOL["bf16"]
+
+
+def test_full_size_swa_prefill_and_decode():
+    """The bench-shaped sliding window (bf16, B=8 H=8 N=4096 d=64, w=64):
+    sampled rows of the prefill against the oracle, then 16 decode steps of
+    all 64 sequences x heads continuing its cache."""
+    _log("full-size swa prefill + decode")
+    B, H, N, d, w, T = 8, 8, 4096, 64, 64, 16
+    q, k, v = synth.draw_qkv(B, H, N + T, d, d, seed=0, dtype="bf16")
+    scale = d ** -0.5
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    sl = lambda x: x[:, :, :N].contiguous()
+    y, (kc, vc) = ops.swa_prefill(sl(qd), sl(kd), sl(vd), w, return_cache=True)
+    pos = torch.full((B,), N, dtype=torch.int64, device=DEV)
+    ys = []
+    for t in range(N, N + T):
+        ys.append(ops.swa_decode_step(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(),
+                                      vd[:, :, t].contiguous(), pos, kc, vc, w))
+        pos += 1
+    torch.cuda.synchronize()
+    y = ops.to_numpy64(y)
+    yd = ops.to_numpy64(torch.stack(ys, dim=2))
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(yd))
+    q64, k64, v64 = q.f64(), k.f64(), v.f64()
+    rng = np.random.default_rng(4)
+    for _ in range(8):
+        b, h = int(rng.integers(0, B)), int(rng.integers(0, H))
+        rows = _sampled_rows(N, rng)
+        ref = oracle.swa_rows(q64[b, h], k64[b, h], v64[b, h], w, scale, rows)
+        assert row_err(y[b, h, rows], ref) <= TOL["bf16"], (b, h)
+        ref = oracle.swa_rows(q64[b, h], k64[b, h], v64[b, h], w, scale,
+                              list(range(N, N + T)))
+        assert row_err(yd[b, h], ref) <= TOL["bf16"], (b, h)
 
 
 @pytest.mark.parametrize("fmap", ["taylor2", "taylor2sym"])
