@@ -13,8 +13,9 @@ per step, all heads).  The same JSON line carries:
                 (algorithmic bytes: state read + written, q, k, v, y);
   cpu_baseline  the float64 oracle on the host, on a bounded sample;
   other_configs the Taylor-2 and 64K-token prefills, an N sweep (4K to
-                64K tokens) showing time linear in N, and the gated
-                (scalar-decay) prefill on the headline and Taylor shapes;
+                64K tokens) showing time linear in N, the gated
+                (scalar-decay) prefill on the headline and Taylor shapes, and
+                sliding-window softmax attention (prefill and generation);
   roofline.intra_chunk_mfma_probe
                 the MFMA rate of the prefill's within-chunk device code on
                 LDS-resident tiles, looped (liblinattn_probe.so).
@@ -208,6 +209,81 @@ def time_decode(args, ops, synth, torch, fmap="taylor2", gated=False):
     return cfg, ms_step, ok, ms_graph
 
 
+def time_swa(args, ops, synth, torch):
+    """Sliding-window softmax attention: the prefill at the headline shape
+    (w = 64) and 128 generation steps after a 1024-token prefill."""
+    dev = "cuda:0"
+    out = {}
+    cfg = synth.WORKLOADS["swa_bf16"]
+    B, H, N, d, w = cfg["B"], cfg["H"], cfg["N"], cfg["d_k"], cfg["window"]
+    q, k, v = synth.workload_inputs("swa_bf16", seed=0)
+    base = [ops.to_device(x, dev) for x in (q, k, v)]
+    nbytes = 4 * B * H * N * d * 2
+    nsets = max(2, -(-ROTATE_BYTES // nbytes))
+    sets = [[t.clone() for t in base] + [torch.empty_like(base[2])] for _ in range(nsets)]
+    L = ops.load_library()
+    stream = ops._stream(base[0])
+    calls = [(1, B, H, N, d, w, d ** -0.5, ops._ptr(s_[0]), ops._ptr(s_[1]), ops._ptr(s_[2]),
+              ops._ptr(s_[3]), None, None, stream) for s_ in sets]
+    for i in range(args.warmup):
+        assert L.linattn_swa_prefill(*calls[i % nsets]) == 0
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    steps = 100
+    ev0.record()
+    for i in range(steps):
+        L.linattn_swa_prefill(*calls[i % nsets])
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    # MFMA work as executed: 2 key blocks of 64 per 64-query tile, scores and
+    # [V | 1] products
+    nt = (N + 63) // 64
+    mfma_flops = B * H * nt * min(nt, (w + 63) // 64 + 1) * 2 * 64 * 64 * (d + d + 16)
+    out["prefill"] = {
+        "workload": f"sliding-window softmax prefill, w={w}, B={B} H={H} N={N} d={d}, bf16",
+        "us_per_call": ms * 1e3, "tokens_per_s": B * N / (ms * 1e-3),
+        "hbm_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+        "mfma_frac_as_executed": mfma_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+    }
+    del sets, base
+
+    dcfg = synth.WORKLOADS["swa_decode_bf16"]
+    B, H, N, d, w, T = (dcfg[x] for x in ("B", "H", "N", "d_k", "window", "steps"))
+    pq, pk, pv, sq, sk, sv = synth.workload_inputs("swa_decode_bf16", seed=0)
+    qd, kd, vd = (ops.to_device(x, dev) for x in (pq, pk, pv))
+    _, (kc, vc) = ops.swa_prefill(qd, kd, vd, w, return_cache=True)
+    del qd, kd, vd
+    st = [ops.to_device(x, dev).permute(2, 0, 1, 3).contiguous() for x in (sq, sk, sv)]
+    y = torch.empty((T, B, H, d), dtype=torch.bfloat16, device=dev)
+    pos = torch.full((B,), N, dtype=torch.int64, device=dev)
+    stepbytes = B * H * (2 * w * d * 2 + 2 * d * 2 + 2 * d * 2) + B * 8
+    dcalls = [(1, B, H, d, w, d ** -0.5, ops._ptr(st[0][t]), ops._ptr(st[1][t]),
+               ops._ptr(st[2][t]), ops._ptr(pos), ops._ptr(kc), ops._ptr(vc), ops._ptr(y[t]),
+               stream) for t in range(T)]
+    for c_ in dcalls:
+        assert L.linattn_swa_decode_step(*c_) == 0
+    torch.cuda.synchronize()
+    reps = max(1, args.decode_reps)
+    ev0.record()
+    for _ in range(reps):
+        for c_ in dcalls:
+            L.linattn_swa_decode_step(*c_)
+    ev1.record()
+    torch.cuda.synchronize()
+    dms = ev0.elapsed_time(ev1) / (reps * T)
+    out["decode"] = {
+        "workload": (f"sliding-window generation step, w={w}, {B} sequences x {H} heads, "
+                     f"d={d}, bf16, cache from a {N}-token prefill"),
+        "ms_per_step": dms, "steps_per_s": 1e3 / dms, "algorithmic_bytes": stepbytes,
+        "hbm_frac": stepbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "finite": bool(torch.isfinite(y.float()).all().item()),
+    }
+    return out
+
+
 def intra_mfma_probe(torch, iters=2000):
     """MFMA rate of the prefill's within-chunk device code on LDS-resident
     bf16 tiles, looped (liblinattn_probe.so): executed MFMA flops / time."""
@@ -244,17 +320,24 @@ def intra_mfma_probe(torch, iters=2000):
     return out
 
 
-def csrc_digest():
-    """Hash of the HIP sources; a traffic figure is valid only for this hash."""
+# Sources that define the kernels behind each recorded traffic figure: the
+# host launch code, the shared device code and the kernels' own files.
+DIGEST_FILES = {
+    "prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp",
+                "prefill_elu1_bf16.hip"),
+    "decode": ("api.hip", "device.hpp", "shapes.hpp", "decode.hip"),
+}
+
+
+def csrc_digest(kind="prefill"):
+    """Hash of the HIP sources of one kernel family; a traffic figure is
+    valid only for this hash."""
     import hashlib
 
     d = hashlib.sha256()
     csrc = os.path.join(ROOT, "causal_linear_attention_linattn_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        path = os.path.join(csrc, name)
-        if not os.path.isfile(path):
-            continue  # the measurement probe (csrc/probe) is not the product
-        with open(path, "rb") as f:
+    for name in DIGEST_FILES[kind]:
+        with open(os.path.join(csrc, name), "rb") as f:
             d.update(name.encode() + b"\0" + f.read())
     return d.hexdigest()[:16]
 
@@ -266,7 +349,7 @@ def recorded_traffic(kind):
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
         return None
-    digest = csrc_digest()
+    digest = csrc_digest(kind)
     for line in open(path):
         parts = line.split()
         if len(parts) == 3 and parts[0] == kind and parts[1] == digest:
@@ -399,6 +482,7 @@ def main():
                                       override={"N": n}, steps=50)
             sweep.append(dict(N=n, **prefill_record(c3, ms3)))
         others["n_sweep_elu1_b1h8_d64_bf16"] = sweep
+        others["sliding_window"] = time_swa(args, ops, synth, torch)
         # the gated (scalar-decay) form on the headline and Taylor shapes
         for name in (PREFILL, "based_taylor2_bf16"):
             c4, ms4, _ = time_prefill(args, ops, synth, torch, name=name, steps=100,

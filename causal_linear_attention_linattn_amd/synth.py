@@ -40,6 +40,13 @@ WORKLOADS = {
     "decode_taylor2_bf16": dict(fmap="taylor2", dtype="bf16", B=256, H=16,
                                 N=1024, steps=128, d_k=16, d_v=64,
                                 qk_scale=1.0),
+    # sliding-window softmax attention (w = 64, d = 64): a prefill of the
+    # headline shape, and generation continuing a 1024-token prefill
+    "swa_bf16": dict(fmap="swa", dtype="bf16", B=8, H=8, N=4096, d_k=64,
+                     d_v=64, window=64, qk_scale=1.0),
+    "swa_decode_bf16": dict(fmap="swa", dtype="bf16", B=256, H=16, N=1024,
+                            steps=128, d_k=64, d_v=64, window=64,
+                            qk_scale=1.0),
 }
 
 
