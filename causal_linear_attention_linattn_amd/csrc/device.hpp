@@ -85,13 +85,58 @@ __device__ __forceinline__ uint32_t buffer_load4(__amdgpu_buffer_rsrc_t r,
 }
 
 // Lane shift inside a wave through DPP (no LDS round trip): lanes whose
-// source is outside the pattern or in a row excluded by ROWS keep `old`.
+// source is outside the pattern or in a row excluded by ROWS keep `old`
+// (or read 0 where the bound-control bit is set).
+//   row_shl:n (0x100 + n)  lane i of a 16-lane row reads lane i + n of it
 //   row_shr:n (0x110 + n)  lane i of a 16-lane row reads lane i - n of it
 //   row_bcast:15 (0x142)   rows 1, 3 read lane 15 of the row before (ROWS 0xa)
 //   row_bcast:31 (0x143)   rows 2, 3 read lane 31 (ROWS 0xc)
 template <int CTRL, int ROWS>
 __device__ __forceinline__ int dpp_move(int old, int v) {
   return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xf, false);
+}
+
+template <int CTRL, int ROWS, bool BOUND>
+__device__ __forceinline__ float dpp_move_f(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v),
+                                                    CTRL, ROWS, 0xf, BOUND));
+}
+
+// Sum of lanes i .. i + G - 1 into lane i, for i a multiple of G (G = 1, 2,
+// 4, 8 or 16: a group inside one 16-lane row); other lanes hold partial
+// sums.  DPP row shifts with out-of-row sources reading 0.
+template <int G>
+__device__ __forceinline__ float group_sum_to_first(float v) {
+  if constexpr (G >= 2) v += dpp_move_f<0x101, 0xf, true>(0.0f, v);
+  if constexpr (G >= 4) v += dpp_move_f<0x102, 0xf, true>(0.0f, v);
+  if constexpr (G >= 8) v += dpp_move_f<0x104, 0xf, true>(0.0f, v);
+  if constexpr (G >= 16) v += dpp_move_f<0x108, 0xf, true>(0.0f, v);
+  static_assert(G >= 1 && G <= 16, "a group inside one row");
+  return v;
+}
+
+// Sum / maximum over the whole wave, returned to every lane: an inclusive
+// scan within each row (row_shr 1, 2, 4, 8), the row totals carried through
+// lanes 15 and 31 (row_bcast), then lane 63's value.  A lane without a
+// source keeps its own value for the maximum and adds 0 for the sum.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_move_f<0x111, 0xf, true>(0.0f, v);
+  v += dpp_move_f<0x112, 0xf, true>(0.0f, v);
+  v += dpp_move_f<0x114, 0xf, true>(0.0f, v);
+  v += dpp_move_f<0x118, 0xf, true>(0.0f, v);
+  v += dpp_move_f<0x142, 0xa, false>(0.0f, v);
+  v += dpp_move_f<0x143, 0xc, false>(0.0f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_move_f<0x111, 0xf, false>(v, v));
+  v = fmaxf(v, dpp_move_f<0x112, 0xf, false>(v, v));
+  v = fmaxf(v, dpp_move_f<0x114, 0xf, false>(v, v));
+  v = fmaxf(v, dpp_move_f<0x118, 0xf, false>(v, v));
+  v = fmaxf(v, dpp_move_f<0x142, 0xa, false>(v, v));
+  v = fmaxf(v, dpp_move_f<0x143, 0xc, false>(v, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // elu(x) + 1 without a compare: exp(x) >= 1 + x for every x (convexity),

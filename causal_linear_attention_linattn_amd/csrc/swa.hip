@@ -100,43 +100,56 @@ __global__ __launch_bounds__(256) void swa_prefill_kernel(const T* __restrict__ 
   constexpr float kNone = -1e30f;  // "minus infinity" that keeps 2^(m - m) = 1
   float m = kNone;
 
-  const int64_t klo = i0 - window + 1 > 0 ? i0 - window + 1 : 0;
-  for (int64_t kb = klo / C; kb <= tile; ++kb) {
-    // ------------------------------------------------ stage block kb ----
+  // Key/value block staging: the next block's global loads are issued into
+  // registers before the current block is computed, so one load latency is
+  // exposed per tile rather than one per block.  bf16: one 16-byte unit per
+  // (row, unit) slot; float: a unit of two consecutive rows (V is stored
+  // transposed, two tokens per LDS store).
+  constexpr int UR = D / EPU;                        // 16-byte units per row
+  constexpr int NU = BF ? C * UR : C / 2 * UR;       // staging slots per tile
+  constexpr int NS = (NU + 255) / 256;               // slots per thread
+  constexpr int NR = BF ? 1 : 2;                     // rows per slot
+  uint4 stk[NS][NR], stv[NS][NR];
+  auto issue = [&](int64_t kb) __attribute__((always_inline)) {
     const uint32_t rb = (uint32_t)(kb * C);  // first key row of the block
-    if constexpr (BF) {
-      constexpr int U = C * D / 8;
 #pragma unroll
-      for (int u = 0; u < (U + 255) / 256; ++u) {
-        const int p = tid + 256 * u;
-        if (U % 256 == 0 || p < U) {
-          const int row = p / RT::UPR, unit = p % RT::UPR;
-          const uint32_t off = ((rb + row) * D + unit * 8) * ES;
-          *reinterpret_cast<uint4*>(sK + RT::off(row, unit)) = buffer_load16(rk, off);
-          *reinterpret_cast<uint4*>(sV + RT::off(row, unit)) = buffer_load16(rv, off);
-        }
-      }
-    } else {
-      constexpr int UR = D / 4;         // 16-byte units per row
-      constexpr int PU = C / 2 * UR;    // row-pair units per tile
+    for (int u = 0; u < NS; ++u) {
+      const int p = tid + 256 * u;
+      const int row = NR * (p / UR), e0 = (p % UR) * EPU;
 #pragma unroll
-      for (int u = 0; u < (PU + 255) / 256; ++u) {
-        const int pu = tid + 256 * u;
-        if (PU % 256 == 0 || pu < PU) {
-          const int r0 = 2 * (pu / UR), e0 = (pu % UR) * 4;
-          const uint32_t off = ((rb + r0) * D + e0) * ES;
-          const uint4 k0 = buffer_load16(rk, off), k1 = buffer_load16(rk, off + D * ES);
-          const uint4 v0 = buffer_load16(rv, off), v1 = buffer_load16(rv, off + D * ES);
-          *reinterpret_cast<uint4*>(sK + r0 * KS + e0) = k0;
-          *reinterpret_cast<uint4*>(sK + (r0 + 1) * KS + e0) = k1;
-          float a[4], b[4];
-          unpack16<T>(v0, a);
-          unpack16<T>(v1, b);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) store_pair(sV + (e0 + e) * CS + r0, a[e], b[e]);
-        }
+      for (int r = 0; r < NR; ++r) {
+        const uint32_t off = NU % 256 == 0 || p < NU ? ((rb + row + r) * D + e0) * ES : kOOB;
+        stk[u][r] = buffer_load16(rk, off);
+        stv[u][r] = buffer_load16(rv, off);
       }
     }
+  };
+  auto write = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int p = tid + 256 * u;
+      if (NU % 256 != 0 && p >= NU) continue;
+      const int row = NR * (p / UR), unit = p % UR, e0 = unit * EPU;
+      if constexpr (BF) {
+        *reinterpret_cast<uint4*>(sK + RT::off(row, unit)) = stk[u][0];
+        *reinterpret_cast<uint4*>(sV + RT::off(row, unit)) = stv[u][0];
+      } else {
+        *reinterpret_cast<uint4*>(sK + row * KS + e0) = stk[u][0];
+        *reinterpret_cast<uint4*>(sK + (row + 1) * KS + e0) = stk[u][1];
+        float a[4], b[4];
+        unpack16<T>(stv[u][0], a);
+        unpack16<T>(stv[u][1], b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_pair(sV + (e0 + e) * CS + row, a[e], b[e]);
+      }
+    }
+  };
+
+  const int64_t klo = i0 - window + 1 > 0 ? i0 - window + 1 : 0;
+  issue(klo / C);
+  for (int64_t kb = klo / C; kb <= tile; ++kb) {
+    write();
+    if (kb < tile) issue(kb + 1);
     lds_barrier();
 
     // --------------------------------- scores^T, band mask, block max ----
@@ -382,11 +395,167 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
   }
 }
 
+// Generation step for windows of at most kSwaSmallWindow slots (the pages
+// use 64 and at most 128).  Every cache row is loaded at entry through a
+// buffer resource over the head's cache (rows past the window read as
+// zero; rows not yet filled are masked by selects, since they may hold
+// anything), together with the query and the new token, so the step waits
+// on HBM once and has no divergent loads.  Partial dot products are summed
+// with DPP row shifts; each wave takes the softmax maximum and sum from the
+// scores in LDS with DPP wave reductions, and each thread exponentiates the
+// scores of its own value rows.  Value partials are summed through LDS.
+constexpr int kSwaSmallWindow = 128;
+
+template <typename T, int D, int NTH>
+__global__ __launch_bounds__(NTH) void swa_decode_small_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int64_t* __restrict__ pos, T* __restrict__ kc, T* __restrict__ vc,
+    T* __restrict__ y, int H, int window, float c) {
+  using E = Elem<T>;
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr uint32_t ES = sizeof(T);
+  constexpr int EPU = E::kPer16B;
+  constexpr int UR = D / EPU;                       // 16-byte units per key row
+  constexpr int NK = kSwaSmallWindow * UR / NTH;    // key units per thread
+  constexpr int CPR = D / 4;                        // 4-column groups per row
+  constexpr int VPP = NTH / CPR;                    // value rows per pass
+  constexpr int NV = kSwaSmallWindow / VPP;         // value groups per thread
+  static_assert(NK >= 1 && NV >= 1 && NTH % UR == 0 && NTH % CPR == 0 && NTH >= D,
+                "tiling");
+  __shared__ float sp[kSwaSmallWindow];
+  __shared__ __align__(16) float red[VPP][D];
+
+  const int bh = blockIdx.x;
+  const int b = bh / H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t p = pos[b];
+  T* yb = y + (size_t)bh * D;
+  if (p < 0) {
+    if (tid < D) yb[tid] = E::from_f32(__builtin_nanf(""));
+    return;
+  }
+  const int slot = (int)(p % window);
+  const int nvalid = p + 1 < window ? (int)(p + 1) : window;
+  const T* kn = k + (size_t)bh * D;
+  const T* vn = v + (size_t)bh * D;
+  T* kcb = kc + (size_t)bh * window * D;
+  T* vcb = vc + (size_t)bh * window * D;
+  const auto rkc = make_rsrc(kcb, (uint32_t)(window * D * ES));
+  const auto rvc = make_rsrc(vcb, (uint32_t)(window * D * ES));
+  const int u = tid % UR;    // this thread's unit of every key row
+  const int cg = tid % CPR;  // and column group of every value row
+  const int ph = tid / CPR;  // and value row phase
+
+  // ------------------------------------------------- every load at once --
+  uint4 kr[NK];
+#pragma unroll
+  for (int i = 0; i < NK; ++i)
+    kr[i] = buffer_load16(rkc, (uint32_t)((((tid + NTH * i) / UR) * D + u * EPU) * ES));
+  uint2 vr2[BF ? NV : 1];
+  uint4 vr4[BF ? 1 : NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint32_t off = (uint32_t)(((ph + VPP * i) * D + 4 * cg) * ES);
+    if constexpr (BF)
+      vr2[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rvc, off, 0, 0));
+    else
+      vr4[i] = buffer_load16(rvc, off);
+  }
+  const uint4 knu = *reinterpret_cast<const uint4*>(kn + u * EPU);
+  float vnf[4];
+  if constexpr (BF) {
+    const uint2 r = *reinterpret_cast<const uint2*>(vn + 4 * cg);
+    vnf[0] = __uint_as_float(r.x << 16);
+    vnf[1] = __uint_as_float(r.x & 0xffff0000u);
+    vnf[2] = __uint_as_float(r.y << 16);
+    vnf[3] = __uint_as_float(r.y & 0xffff0000u);
+  } else {
+    const float4 r = *reinterpret_cast<const float4*>(vn + 4 * cg);
+    vnf[0] = r.x; vnf[1] = r.y; vnf[2] = r.z; vnf[3] = r.w;
+  }
+  float qf[EPU];
+  unpack16<T>(*reinterpret_cast<const uint4*>(q + (size_t)bh * D + u * EPU), qf);
+
+  // ------------------------------------------------------------ scores --
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int j = (tid + NTH * i) / UR;
+    float kf[EPU];
+    unpack16<T>(j == slot ? knu : kr[i], kf);
+    float part = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) part += qf[e] * kf[e];
+    if constexpr (UR <= 16) {
+      part = group_sum_to_first<UR>(part);
+    } else {
+      part = group_sum_to_first<16>(part);
+      part += __shfl_down(part, 16, 64);
+    }
+    if (u == 0) sp[j] = j < nvalid ? part * c : -1e30f;
+  }
+  lds_barrier();
+
+  // softmax statistics, per wave (every slot index is below 128)
+  const float s0 = sp[lane], s1 = sp[lane + 64];
+  const float mx = wave_max(fmaxf(s0, s1));
+  const float sum = wave_sum((lane < nvalid ? __builtin_amdgcn_exp2f(s0 - mx) : 0.0f) +
+                             (lane + 64 < nvalid ? __builtin_amdgcn_exp2f(s1 - mx) : 0.0f));
+
+  // ------------------------------------------------------------ values --
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int j = ph + VPP * i;
+    float vf[4];
+    if (j == slot) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vf[e] = vnf[e];
+    } else if constexpr (BF) {
+      vf[0] = __uint_as_float(vr2[i].x << 16);
+      vf[1] = __uint_as_float(vr2[i].x & 0xffff0000u);
+      vf[2] = __uint_as_float(vr2[i].y << 16);
+      vf[3] = __uint_as_float(vr2[i].y & 0xffff0000u);
+    } else {
+      vf[0] = __uint_as_float(vr4[i].x);
+      vf[1] = __uint_as_float(vr4[i].y);
+      vf[2] = __uint_as_float(vr4[i].z);
+      vf[3] = __uint_as_float(vr4[i].w);
+    }
+    const float pj = __builtin_amdgcn_exp2f(sp[j] - mx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += j < nvalid ? pj * vf[e] : 0.0f;
+  }
+  *reinterpret_cast<float4*>(&red[ph][4 * cg]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  // the new token into its slot (no thread reads that slot from the cache)
+  if (tid < UR) {
+    *reinterpret_cast<uint4*>(kcb + (size_t)slot * D + tid * EPU) = knu;
+    *reinterpret_cast<uint4*>(vcb + (size_t)slot * D + tid * EPU) =
+        *reinterpret_cast<const uint4*>(vn + tid * EPU);
+  }
+  lds_barrier();
+  if (tid < D) {
+    float o = 0.0f;
+#pragma unroll
+    for (int r = 0; r < VPP; ++r) o += red[r][tid];
+    yb[tid] = E::from_f32(o * fast_rcp(sum));
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_swa_decode(const void* q, const void* k, const void* v,
                              const int64_t* pos, void* kc, void* vc, void* y,
                              int64_t B, int64_t H, int64_t window, float scale,
                              hipStream_t st) {
+  if (window <= kSwaSmallWindow) {
+    constexpr int NTH = 256;
+    hipLaunchKernelGGL((swa_decode_small_kernel<T, D, NTH>), dim3((unsigned)(B * H)), dim3(NTH), 0,
+                       st, reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k),
+                       reinterpret_cast<const T*>(v), pos, reinterpret_cast<T*>(kc),
+                       reinterpret_cast<T*>(vc), reinterpret_cast<T*>(y), (int)H, (int)window,
+                       scale * kLog2e);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((swa_decode_kernel<T, D>), dim3((unsigned)(B * H)), dim3(256), 0, st,
                      reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k),
                      reinterpret_cast<const T*>(v), pos, reinterpret_cast<T*>(kc),

@@ -447,10 +447,13 @@ def test_swa_prefill_small(d, dtype, N, w):
 
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("w,P", [(64, 100), (16, 5), (100, 40)])
+@pytest.mark.parametrize("w,P", [(64, 100), (16, 5), (100, 40), (128, 130), (200, 300),
+                                 (1000, 50)])
 def test_swa_decode_continues_prefill(d, dtype, w, P):
     """Prefill P tokens (writing the caches), then 12 decode steps: every
-    step's output equals the oracle's dense form over all P + 12 tokens."""
+    step's output equals the oracle's dense form over all P + 12 tokens.
+    Windows up to 128 take the preloading step kernel, larger ones the
+    looping one."""
     _log(f"swa_decode d={d} {dtype} w={w} P={P}")
     B, H, T = 2, 3, 12
     q, k, v = synth.draw_qkv(B, H, P + T, d, d, seed=7 + w, dtype=dtype)
