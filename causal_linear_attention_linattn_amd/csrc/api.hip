@@ -136,16 +136,34 @@ bool plan_segments(int64_t BH, int64_t N, int64_t seg_len, int64_t row_bytes,
   return true;
 }
 
-// Workspace: BH * nseg slots of partial states, then one float per slot
-// (the log2 decay of a segment in gated calls), padded to 16 bytes.
-size_t slots_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nseg) {
-  return (size_t)BH * (size_t)nseg * (size_t)slot_floats(map, dk, dv) * 4u;
+// The segment-sum pass of the Taylor maps (18 state row tiles per chunk)
+// splits each segment into `sum_split` parts when the heads are too few for
+// one workgroup per segment to occupy the GPU twice over, as long as a part
+// keeps kMinSumChunks chunks: measured on one MI355X at B=8 H=16 N=2048,
+// 117 -> 111 us per call.  For ELU1 the extra prefix slots the output
+// workgroups then add cost more than the shorter pass saves (43.5 -> 45.6 us
+// at B=8 H=8 N=4096 d=64), so it keeps one part.
+constexpr int64_t kMinSumChunks = 4;
+
+int sum_split(int map, int64_t BH, int nseg, int seg_chunks) {
+  if (map == LINATTN_MAP_ELU1 || nseg <= 1) return 1;
+  if (BH * (nseg - 1) >= 2 * kTargetWorkgroups) return 1;
+  if (seg_chunks % 2 != 0 || seg_chunks / 2 < kMinSumChunks) return 1;
+  return 2;
 }
 
-size_t workspace_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nseg) {
+// Workspace: BH * nseg * sum_split slots of partial states, then one float
+// per slot (the log2 decay of a part in gated calls), padded to 16 bytes.
+size_t slots_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nslot) {
+  return (size_t)BH * (size_t)nslot * (size_t)slot_floats(map, dk, dv) * 4u;
+}
+
+size_t workspace_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nseg,
+                       int seg_chunks) {
   if (nseg <= 1) return 0;
-  const size_t logs = ((size_t)BH * (size_t)nseg * 4u + 15u) & ~(size_t)15u;
-  return slots_bytes(map, BH, dk, dv, nseg) + logs;
+  const int nslot = nseg * sum_split(map, BH, nseg, seg_chunks);
+  const size_t logs = ((size_t)BH * (size_t)nslot * 4u + 15u) & ~(size_t)15u;
+  return slots_bytes(map, BH, dk, dv, nslot) + logs;
 }
 
 template <bool GATED>
@@ -231,7 +249,7 @@ linattn_status_t prefill_common(int map, int dtype, int64_t B, int64_t H,
   for (int i = 0; i < 3; ++i)
     if (overlap(outs[i], rg)) return LINATTN_ERR_INVALID_ARGUMENT;
 
-  const size_t need = workspace_bytes(map, BH, d_k, d_v, nseg);
+  const size_t need = workspace_bytes(map, BH, d_k, d_v, nseg, seg_chunks);
   if (need > 0) {
     if (workspace == nullptr || !aligned16(workspace) || workspace_bytes_given < need)
       return LINATTN_ERR_WORKSPACE;
@@ -255,11 +273,14 @@ linattn_status_t prefill_common(int map, int dtype, int64_t B, int64_t H,
   a.BH = (int)BH;
   a.nseg = nseg;
   a.seg_chunks = seg_chunks;
-  a.prefix_mode = nseg == 1 ? 0 : (nseg <= kDirectPrefixMax ? 1 : 2);
+  a.sum_split = sum_split(map, BH, nseg, seg_chunks);
+  a.nslot = nseg * a.sum_split;
+  a.prefix_mode =
+      nseg == 1 ? 0 : ((nseg - 1) * a.sum_split <= kDirectPrefixMax - 1 ? 1 : 2);
   a.sym = map == LINATTN_MAP_TAYLOR2_SYM ? 1 : 0;
   a.gate = gated ? gate : nullptr;
   a.ws_log = gated && nseg > 1
-                 ? a.ws + slots_bytes(map, BH, d_k, d_v, nseg) / sizeof(float)
+                 ? a.ws + slots_bytes(map, BH, d_k, d_v, a.nslot) / sizeof(float)
                  : nullptr;
   a.normalize = gated ? normalize : 1;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -411,7 +432,7 @@ size_t linattn_prefill_workspace_bytes(int map, int dtype, int64_t B, int64_t H,
   int nseg, seg_chunks;
   const int64_t row_bytes = (d_k > d_v ? d_k : d_v) * (int64_t)elem_size(dtype);
   if (!plan_segments(B * H, N, seg_len, row_bytes, &nseg, &seg_chunks)) return (size_t)-1;
-  return workspace_bytes(map, B * H, d_k, d_v, nseg);
+  return workspace_bytes(map, B * H, d_k, d_v, nseg, seg_chunks);
 }
 
 linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,

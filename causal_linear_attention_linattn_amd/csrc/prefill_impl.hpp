@@ -380,12 +380,15 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   const int i16 = lane & 15;
   const int g = lane >> 4;
 
-  const int nseg_here = OUT ? a.nseg : a.nseg - 1;
+  // OUT: one workgroup per output segment.  Segment sums: one per part of
+  // every segment but the last (sum_split parts per segment).
+  const int nseg_here = OUT ? a.nseg : (a.nseg - 1) * a.sum_split;
+  const int seg_chunks = OUT ? a.seg_chunks : a.seg_chunks / a.sum_split;
   const int bh = blockIdx.x / nseg_here;
   const int seg = blockIdx.x % nseg_here;
   const int64_t N = a.N;
-  const int64_t tok_begin = (int64_t)seg * a.seg_chunks * C;
-  int64_t tok_end = tok_begin + (int64_t)a.seg_chunks * C;
+  const int64_t tok_begin = (int64_t)seg * seg_chunks * C;
+  int64_t tok_end = tok_begin + (int64_t)seg_chunks * C;
   if (tok_end > N) tok_end = N;
   const int ntok = (int)(tok_end - tok_begin);   // tokens in this segment
   const int nchunks = (ntok + C - 1) / C;
@@ -411,9 +414,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
       if (OUT && rt < NRT) {
         if (a.prefix_mode == 2) {
-          // scanned workspace: slot seg holds the exclusive prefix
+          // scanned workspace: slot seg * sum_split holds the exclusive
+          // prefix of the segment
           const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
-              a.ws + ((size_t)bh * a.nseg + seg) * SH::SLOT);
+              a.ws + ((size_t)bh * a.nslot + seg * a.sum_split) * SH::SLOT);
           s = p[(rt * NCT + ct) * 64 + lane];
         } else if (a.S_in != nullptr) {
           s = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, a.sym != 0, bh, rt, ct,
@@ -433,10 +437,11 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     // Gated: the state entering segment j + 1 is the one entering segment j
     // scaled by segment j's total decay, plus segment j's own sum; the
     // log2 decays past `seg` read as 0 (factor 1).
-    const auto rw = make_rsrc(a.ws + ((size_t)bh * a.nseg + 1) * SH::SLOT,
-                              (uint32_t)seg * SH::SLOT * 4u);
-    const auto rl = make_rsrc(GATED ? a.ws_log + (size_t)bh * a.nseg + 1 : nullptr,
-                              GATED ? (uint32_t)seg * 4u : 0u);
+    const int npre = seg * a.sum_split;  // sums of the parts before seg
+    const auto rw = make_rsrc(a.ws + ((size_t)bh * a.nslot + 1) * SH::SLOT,
+                              (uint32_t)npre * SH::SLOT * 4u);
+    const auto rl = make_rsrc(GATED ? a.ws_log + (size_t)bh * a.nslot + 1 : nullptr,
+                              GATED ? (uint32_t)npre * 4u : 0u);
 #pragma unroll
     for (int j = 0; j < kDirectPrefixMax - 1; ++j) {
       float fj = 1.0f;
@@ -1012,7 +1017,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     }
   } else {
     f32x4_t* p = reinterpret_cast<f32x4_t*>(
-        a.ws + ((size_t)bh * a.nseg + seg + 1) * SH::SLOT);
+        a.ws + ((size_t)bh * a.nslot + seg + 1) * SH::SLOT);
 #pragma unroll
     for (int m = 0; m < SH::MAXRT; ++m) {
       const int rt = w + 4 * m;
@@ -1021,13 +1026,14 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       for (int ct = 0; ct < NCT; ++ct) p[(rt * NCT + ct) * 64 + lane] = Sacc[m][ct];
     }
     if constexpr (GATED) {
-      if (tid == 0) a.ws_log[(size_t)bh * a.nseg + seg + 1] = seg_log;
+      if (tid == 0) a.ws_log[(size_t)bh * a.nslot + seg + 1] = seg_log;
     }
   }
 }
 
-// Exclusive prefix over segments, in place: slot s <- init + sum_{p<s} T_p,
-// where slot p+1 held segment p's sum T_p and init is the initial state.
+// Exclusive prefix over the summed parts, in place: slot s <- init +
+// sum_{p<s} T_p, where slot p+1 held part p's sum T_p and init is the
+// initial state (output segment s then reads slot s * sum_split).
 // Gated form: slot s <- 2^l_s slot(s-1) + T_(s-1), with l_s the log2 decay of
 // segment s - 1 (ws_log).  Used when there are too many segments per head for
 // each output workgroup to add up its predecessors' sums itself.
@@ -1046,19 +1052,20 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(PrefillArgs a) {
     run = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, a.sym != 0, bh, rt, ct,
                                     e4 % 64);
   }
-  f32x4_t* p = reinterpret_cast<f32x4_t*>(a.ws + (size_t)bh * a.nseg * SS::SLOT) + e4;
-  const float* lg = a.ws_log != nullptr ? a.ws_log + (size_t)bh * a.nseg : nullptr;
+  f32x4_t* p = reinterpret_cast<f32x4_t*>(a.ws + (size_t)bh * a.nslot * SS::SLOT) + e4;
+  const float* lg = a.ws_log != nullptr ? a.ws_log + (size_t)bh * a.nslot : nullptr;
+  const int nscan = (a.nseg - 1) * a.sum_split + 1;  // slot 0 and every sum
   p[0] = run;
   // batches of 16 slots: all loads of a batch are in flight at once
   constexpr int kB = 16;
-  for (int s0 = 1; s0 < a.nseg; s0 += kB) {
+  for (int s0 = 1; s0 < nscan; s0 += kB) {
     f32x4_t t[kB];
 #pragma unroll
     for (int j = 0; j < kB; ++j)
-      if (s0 + j < a.nseg) t[j] = p[(size_t)(s0 + j) * Q];
+      if (s0 + j < nscan) t[j] = p[(size_t)(s0 + j) * Q];
 #pragma unroll
     for (int j = 0; j < kB; ++j)
-      if (s0 + j < a.nseg) {
+      if (s0 + j < nscan) {
         if (lg != nullptr) run *= __builtin_amdgcn_exp2f(lg[s0 + j]);
         run += t[j];
         p[(size_t)(s0 + j) * Q] = run;
@@ -1071,7 +1078,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   using SS = StateShape<MAP, DK, DV>;
   if (a.nseg > 1) {
     hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, false, GATED>),
-                       dim3(a.BH * (a.nseg - 1)), dim3(256), 0, st, a);
+                       dim3(a.BH * (a.nseg - 1) * a.sum_split), dim3(256), 0, st, a);
     if (a.prefix_mode == 2) {
       const int64_t threads = (int64_t)a.BH * (SS::SLOT / 4);
       hipLaunchKernelGGL((seg_scan_kernel<MAP, DK, DV>),

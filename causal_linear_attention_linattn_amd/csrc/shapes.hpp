@@ -17,9 +17,9 @@ enum { MAP_ELU1 = 0, MAP_TAYLOR2 = 1, MAP_TAYLOR2_SYM = 2 };
 template <int DK>
 constexpr int kSymD = 1 + DK + DK * (DK + 1) / 2;
 
-// Most segments per head for which each output workgroup adds up the sums
-// of its preceding segments itself (prefix_mode 1); beyond it a scan kernel
-// forms the prefixes (prefix_mode 2).
+// Output workgroups add the sums of the parts before their segment
+// themselves (prefix_mode 1) while there are fewer than kDirectPrefixMax of
+// them; beyond that a scan kernel forms the prefixes (prefix_mode 2).
 constexpr int kDirectPrefixMax = 8;
 
 struct PrefillArgs {
@@ -38,6 +38,9 @@ struct PrefillArgs {
   int seg_chunks;  // chunks per segment
   int prefix_mode; // 0: one segment; 1: output workgroups add the preceding
                    // segment sums themselves; 2: a scan kernel runs first
+  int sum_split;   // the segment-sum pass splits each segment into this many
+                   // equal parts (more, shorter workgroups when heads are few)
+  int nslot;       // workspace slots per (batch, head): nseg * sum_split
   int sym;         // MAP_TAYLOR2 only: S_in/S_out use the unordered-pair
                    // layout (kSymD rows) instead of the ordered one
   // Gated (scalar-decay) calls only: the decay coefficients a [BH, N], the

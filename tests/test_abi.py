@@ -99,10 +99,17 @@ def test_workspace_bytes(lib):
     slot_elu64 = 4 * 5 * 256
     assert f(0, 1, 8, 8, 4096, 64, 64, 1024) == 64 * 4 * slot_elu64 * 4 + logs(64 * 4)
     assert f(0, 1, 8, 8, 4096, 64, 64, 4096) == 0
+    # With few heads the Taylor segment-sum pass splits each segment in two
+    # (B*H*(nseg-1) below 512 workgroups and halves of >= 4 chunks),
+    # doubling the slots; ELU1 never splits.
     slot_tay = 18 * 5 * 256
-    assert f(1, 1, 8, 16, 2048, 16, 64, 512) == 128 * 4 * slot_tay * 4 + logs(128 * 4)
+    # 512 heads x 3 summed segments fill the GPU already: no split
+    assert f(1, 1, 64, 8, 2048, 16, 64, 512) == 512 * 4 * slot_tay * 4 + logs(512 * 4)
+    # 6-chunk segments would leave 3-chunk halves: no split
+    assert f(1, 1, 1, 2, 4096, 16, 16, 384) == 2 * 11 * (18 * 2 * 256) * 4 + logs(2 * 11)
+    assert f(1, 1, 8, 16, 2048, 16, 64, 512) == 128 * 8 * slot_tay * 4 + logs(128 * 8)
     # the unordered-pair map runs on the same kernels and workspace
-    assert f(2, 1, 8, 16, 2048, 16, 64, 512) == 128 * 4 * slot_tay * 4 + logs(128 * 4)
+    assert f(2, 1, 8, 16, 2048, 16, 64, 512) == 128 * 8 * slot_tay * 4 + logs(128 * 8)
     # ragged: 65 tokens in 64-token segments -> 2 segments
     assert f(0, 0, 1, 1, 65, 16, 16, 64) == 2 * (2 * 2 * 256) * 4 + 16
     assert f(0, 1, 1, 1, 4096, 64, 64, 100) == bad     # not a multiple of 64
