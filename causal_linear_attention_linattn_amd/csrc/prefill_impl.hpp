@@ -16,9 +16,10 @@
 // fp32 MFMA for float inputs); the state S' stays in fp32 accumulators.
 //
 // Parallel layout.  A workgroup of 4 waves owns one (batch*head, segment):
-// a run of consecutive chunks walked in order.  Wave w produces the outputs
-// of the chunk's 16-token tile w (all value columns) and owns state row
-// tiles w, w+4, w+8, ... (16 features each) across all columns.  A bf16 (or
+// a run of consecutive chunks walked in order.  Waves 0..3 produce the
+// outputs of the chunk's 16-token tiles (all value columns); every wave w of
+// the NW owns state row tiles w, w+NW, w+2NW, ... (16 features each) across
+// all columns.  NW = 4, or 8 for the bf16 Taylor state (kChunkWaves).  A bf16 (or
 // fp32) copy of S' in LDS, laid out column-major, feeds the inter term of
 // every wave.  K, V tiles are staged through LDS transposed (feature- and
 // value-major) so that every MFMA operand is one 16-byte LDS read; the next
@@ -42,11 +43,19 @@
 
 namespace linattn {
 
-template <int MAP, typename T, int DK, int DV>
+// Waves per chunk workgroup.  The Taylor state (18 row tiles) is spread
+// over 8 waves for bf16 inputs without decay, so that each holds fewer
+// accumulators and two waves share a SIMD (measured on one MI355X at
+// B=8 H=16 N=2048: 111.7 -> 106.6 us per call); with the decay factors or
+// float tiles the 8-wave build spills (gated: 130 -> 150 us), so those keep 4.
+template <int MAP, typename T, bool GATED>
+constexpr int kChunkWaves = MAP != MAP_ELU1 && sizeof(T) == 2 && !GATED ? 8 : 4;
+
+template <int MAP, typename T, int DK, int DV, int NWAVES = 4>
 struct PrefillShape : StateShape<MAP, DK, DV> {
   using SS = StateShape<MAP, DK, DV>;
   static constexpr int C = 64;
-  static constexpr int NW = 4;
+  static constexpr int NW = NWAVES;  // waves per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int MAXRT = (SS::NRT + NW - 1) / NW;
   static constexpr int EPU = Elem<T>::kPer16B;
@@ -323,8 +332,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int MAP, typename T, int DK, int DV, bool OUT, bool GATED>
-__global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
-  using SH = PrefillShape<MAP, T, DK, DV>;
+__global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kernel(PrefillArgs a) {
+  using SH = PrefillShape<MAP, T, DK, DV, kChunkWaves<MAP, T, GATED>>;
   using E = Elem<T>;
   using frag = typename E::frag;
   constexpr bool BF = sizeof(T) == 2;
@@ -375,7 +384,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   auto sS = [&](int b) __attribute__((always_inline)) { return (NSB == 2 && b) ? sS1 : sS0; };
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;  // wave-uniform, 0..3
+  constexpr int NW = SH::NW;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1);  // wave-uniform
+  // waves that own one of the chunk's 4 query tiles (all of them when NW = 4)
+  const bool qwave = NW == 4 || w < 4;
   const int lane = tid & 63;
   const int i16 = lane & 15;
   const int g = lane >> 4;
@@ -408,7 +420,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   f32x4_t Sacc[SH::MAXRT][NCT];
 #pragma unroll
   for (int m = 0; m < SH::MAXRT; ++m) {
-    const int rt = w + 4 * m;
+    const int rt = w + NW * m;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -449,7 +461,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
         fj = __builtin_amdgcn_exp2f(__uint_as_float(buffer_load4(rl, (uint32_t)j * 4u)));
 #pragma unroll
       for (int m = 0; m < SH::MAXRT; ++m) {
-        const int rt = w + 4 * m;
+        const int rt = w + NW * m;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const uint32_t off = rt < NRT ? ((uint32_t)j * SH::SLOT + ((rt * NCT + ct) * 64 + lane) * 4) * 4u
@@ -516,7 +528,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
         s.v[2 * u + 1] = buffer_load16(rv, pu < SH::PV ? off + DV * ES : kOOB);
       }
     }
-    if constexpr (OUT) {
+    if constexpr (OUT) if (qwave) {
       const uint32_t tq = cb + 16 * w + i16;
       if constexpr (MAP == MAP_ELU1) {
         constexpr int UPB = 8 / EPU;  // 16-byte units per 8-feature block
@@ -660,6 +672,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 
   auto take_q = [&](const St& s, int b) __attribute__((always_inline)) {
     if constexpr (!OUT) return;
+    if (!qwave) return;
     if constexpr (MAP == MAP_ELU1) {
       constexpr int UPB = 8 / EPU;
 #pragma unroll
@@ -769,7 +782,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
   auto publish_state = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < SH::MAXRT; ++m) {
-      const int rt = w + 4 * m;
+      const int rt = w + NW * m;
       if (rt >= NRT) continue;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -821,9 +834,11 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       fc = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
                                          __builtin_bit_cast(int, sF[b][C - 1])));
       if constexpr (OUT) {
-        Gq = sG[b][il];
-        Lq = sL[b][il];
-        fq = sF[b][il];
+        if (qwave) {
+          Gq = sG[b][il];
+          Lq = sL[b][il];
+          fq = sF[b][il];
+        }
       } else {
         const float Ge = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
                                                        __builtin_bit_cast(int, sG[b][C - 1])));
@@ -834,7 +849,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
 
     f32x4_t O[OUT ? NCT : 1];
     frag qraw = E::zero();
-    if constexpr (OUT) {
+    if constexpr (OUT) if (qwave) {
       if constexpr (MAP == MAP_TAYLOR2) {
 #pragma unroll
         for (int u = 0; u < SH::NQU; ++u) {
@@ -908,7 +923,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
         u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
       }
 
-      if constexpr (OUT) {
+      if constexpr (OUT) if (qwave) {
         // within-chunk term: scores^T of this key block against the wave's
         // queries (key blocks wholly after them come out fully masked)
         frag bq[SH::NKBS];
@@ -923,7 +938,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       // state update: S' += phi(K)^T V' for this wave's row tiles
 #pragma unroll
       for (int m = 0; m < SH::MAXRT; ++m) {
-        const int rt = w + 4 * m;
+        const int rt = w + NW * m;
         if (rt >= NRT) continue;
         const frag ak = kt_frag(b, rt, jb2, u);
 #pragma unroll
@@ -932,7 +947,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
       }
     }
 
-    if constexpr (OUT) {
+    if constexpr (OUT) if (qwave) {
       // normalise and write y (query il of this chunk; rows past the
       // segment end fall outside the store range)
       const float den = __shfl(O[NCT - 1][0], i16, 64);
@@ -952,6 +967,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, d), ry, off, 0, 0);
         }
       }
+    }
+    if constexpr (OUT) {
       // state through chunk c for the prefix term of chunk c + 1
       if constexpr (NSB == 1) lds_barrier();  // every wave is done with sS
       publish_state(1 - b);
@@ -992,7 +1009,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     const float n_pad = (float)(((nchunks + P - 1) / P) * P * C - ntok);
 #pragma unroll
     for (int m = 0; m < SH::MAXRT; ++m) {
-      const int rt = w + 4 * m;
+      const int rt = w + NW * m;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int row = 16 * rt + 4 * g + t;
@@ -1007,7 +1024,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
     if (seg == a.nseg - 1 && a.S_out != nullptr) {
 #pragma unroll
       for (int m = 0; m < SH::MAXRT; ++m) {
-        const int rt = w + 4 * m;
+        const int rt = w + NW * m;
         if (rt >= NRT) continue;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -1020,7 +1037,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a) {
         a.ws + ((size_t)bh * a.nslot + seg + 1) * SH::SLOT);
 #pragma unroll
     for (int m = 0; m < SH::MAXRT; ++m) {
-      const int rt = w + 4 * m;
+      const int rt = w + NW * m;
       if (rt >= NRT) continue;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) p[(rt * NCT + ct) * 64 + lane] = Sacc[m][ct];
@@ -1076,9 +1093,10 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(PrefillArgs a) {
 template <int MAP, typename T, int DK, int DV, bool GATED>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   using SS = StateShape<MAP, DK, DV>;
+  constexpr int NT = 64 * kChunkWaves<MAP, T, GATED>;
   if (a.nseg > 1) {
     hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, false, GATED>),
-                       dim3(a.BH * (a.nseg - 1) * a.sum_split), dim3(256), 0, st, a);
+                       dim3(a.BH * (a.nseg - 1) * a.sum_split), dim3(NT), 0, st, a);
     if (a.prefix_mode == 2) {
       const int64_t threads = (int64_t)a.BH * (SS::SLOT / 4);
       hipLaunchKernelGGL((seg_scan_kernel<MAP, DK, DV>),
@@ -1087,7 +1105,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     }
   }
   hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, true, GATED>),
-                     dim3(a.BH * a.nseg), dim3(256), 0, st, a);
+                     dim3(a.BH * a.nseg), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
