@@ -449,6 +449,28 @@ def test_swa_prefill_small(d, dtype, N, w):
     assert np.array_equal(ops.to_numpy64(vc), vc_ref)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("w", [64, 100])
+def test_swa_prefill_long_runs(dtype, w):
+    """B=1 H=2 N=70000 (a ragged last tile), w spanning 2 and 3 key blocks
+    per tile: rows at the start, around tile boundaries, at the end and a
+    random sample against the oracle's single rows."""
+    _log(f"swa_prefill long runs {dtype} w={w}")
+    d, N = 64, 70000
+    q, k, v = synth.draw_qkv(1, 2, N, d, d, seed=w, dtype=dtype)
+    scale = d ** -0.5
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    y = ops.to_numpy64(ops.swa_prefill(qd, kd, vd, w))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w)
+    rows = sorted(set(list(range(0, 130)) + list(range(300, 340)) + list(range(635, 645))
+                      + list(range(N - 70, N)) + rng.integers(0, N, 60).tolist()))
+    q64, k64, v64 = q.f64(), k.f64(), v.f64()
+    for h in range(2):
+        ref = oracle.swa_rows(q64[0, h], k64[0, h], v64[0, h], w, scale, rows)
+        assert row_err(y[0, h, rows], ref) <= TOL[dtype], h
+
+
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("w,P", [(64, 100), (16, 5), (100, 40), (128, 130), (200, 300),
