@@ -212,8 +212,12 @@ def time_decode(args, ops, synth, torch, fmap="taylor2", gated=False):
 def time_swa(args, ops, synth, torch):
     """Sliding-window softmax attention: the prefill at the headline shape
     (w = 64) and 128 generation steps after a 1024-token prefill."""
+    return {"prefill": time_swa_prefill(args, ops, synth, torch),
+            "decode": time_swa_decode(args, ops, synth, torch)}
+
+
+def time_swa_prefill(args, ops, synth, torch):
     dev = "cuda:0"
-    out = {}
     cfg = synth.WORKLOADS["swa_bf16"]
     B, H, N, d, w = cfg["B"], cfg["H"], cfg["N"], cfg["d_k"], cfg["window"]
     q, k, v = synth.workload_inputs("swa_bf16", seed=0)
@@ -242,20 +246,29 @@ def time_swa(args, ops, synth, torch):
     # [V | 1] products
     nt = (N + 63) // 64
     mfma_flops = B * H * nt * min(nt, (w + 63) // 64 + 1) * 2 * 64 * 64 * (d + d + 16)
-    out["prefill"] = {
+    rec = {
         "workload": f"sliding-window softmax prefill, w={w}, B={B} H={H} N={N} d={d}, bf16",
         "us_per_call": ms * 1e3, "tokens_per_s": B * N / (ms * 1e-3),
         "hbm_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+        "traffic": recorded_traffic("swa_prefill"),
         "mfma_frac_as_executed": mfma_flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
     }
     del sets, base
+    return rec
 
+
+def time_swa_decode(args, ops, synth, torch):
+    dev = "cuda:0"
+    L = ops.load_library()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     dcfg = synth.WORKLOADS["swa_decode_bf16"]
     B, H, N, d, w, T = (dcfg[x] for x in ("B", "H", "N", "d_k", "window", "steps"))
     pq, pk, pv, sq, sk, sv = synth.workload_inputs("swa_decode_bf16", seed=0)
     qd, kd, vd = (ops.to_device(x, dev) for x in (pq, pk, pv))
     _, (kc, vc) = ops.swa_prefill(qd, kd, vd, w, return_cache=True)
     del qd, kd, vd
+    stream = ops._stream(kc)
     st = [ops.to_device(x, dev).permute(2, 0, 1, 3).contiguous() for x in (sq, sk, sv)]
     y = torch.empty((T, B, H, d), dtype=torch.bfloat16, device=dev)
     pos = torch.full((B,), N, dtype=torch.int64, device=dev)
@@ -274,14 +287,14 @@ def time_swa(args, ops, synth, torch):
     ev1.record()
     torch.cuda.synchronize()
     dms = ev0.elapsed_time(ev1) / (reps * T)
-    out["decode"] = {
+    return {
         "workload": (f"sliding-window generation step, w={w}, {B} sequences x {H} heads, "
                      f"d={d}, bf16, cache from a {N}-token prefill"),
         "ms_per_step": dms, "steps_per_s": 1e3 / dms, "algorithmic_bytes": stepbytes,
         "hbm_frac": stepbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "traffic": recorded_traffic("swa_decode"),
         "finite": bool(torch.isfinite(y.float()).all().item()),
     }
-    return out
 
 
 def intra_mfma_probe(torch, iters=2000):
@@ -326,6 +339,12 @@ DIGEST_FILES = {
     "prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp",
                 "prefill_elu1_bf16.hip"),
     "decode": ("api.hip", "device.hpp", "shapes.hpp", "decode.hip"),
+    "taylor2_prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp",
+                        "prefill_taylor2_bf16.hip"),
+    "gated_prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp",
+                      "prefill_elu1_bf16_gated.hip"),
+    "swa_prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp", "swa.hip"),
+    "swa_decode": ("api.hip", "device.hpp", "shapes.hpp", "swa.hip"),
 }
 
 
@@ -443,6 +462,10 @@ def main():
                     help="skip the Taylor / long-sequence prefills and the N sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy used to scale HBM counters")
+    ap.add_argument("--only", choices=("taylor2_prefill", "gated_prefill", "swa_prefill",
+                                       "swa_decode"),
+                    help="time one secondary section alone and print its record "
+                         "(for per-kernel profiles of that section)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -467,6 +490,20 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
         return
+    if args.only:
+        if args.only == "taylor2_prefill":
+            c, m_, _ = time_prefill(args, ops, synth, torch, name="based_taylor2_bf16")
+            rec = prefill_record(c, m_)
+        elif args.only == "gated_prefill":
+            c, m_, _ = time_prefill(args, ops, synth, torch, gated=True)
+            rec = prefill_record(c, m_)
+        elif args.only == "swa_prefill":
+            rec = time_swa_prefill(args, ops, synth, torch)
+        else:
+            rec = time_swa_decode(args, ops, synth, torch)
+        rec["traffic"] = recorded_traffic(args.only)
+        print(json.dumps({"section": args.only, **rec}), flush=True)
+        return
 
     cfg, ms, nsets = time_prefill(args, ops, synth, torch)
     others = {}
@@ -478,6 +515,7 @@ def main():
                                 workload=(f"prefill {c2['fmap']} B={c2['B']} H={c2['H']} "
                                           f"N={c2['N']} d_k={c2['d_k']} d_v={c2['d_v']} "
                                           f"{c2['dtype']}"))
+        others["based_taylor2_bf16"]["traffic"] = recorded_traffic("taylor2_prefill")
         # linear in N: ELU1 bf16, B=1 H=8 d=64, N from 4K to 64K
         sweep = []
         for n in (4096, 8192, 16384, 32768, 65536):
@@ -495,6 +533,7 @@ def main():
                 workload=(f"gated prefill (a in [0.9, 1), 0.1% resets) {c4['fmap']} "
                           f"B={c4['B']} H={c4['H']} N={c4['N']} d_k={c4['d_k']} "
                           f"d_v={c4['d_v']} {c4['dtype']}"))
+        others["gated_" + PREFILL]["traffic"] = recorded_traffic("gated_prefill")
     tokens = cfg["B"] * cfg["N"]
     nbytes = prefill_bytes(cfg)
     flops = prefill_flops(cfg)
