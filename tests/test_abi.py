@@ -202,3 +202,57 @@ def test_decode_and_feature_map_validation(lib):
     assert g(1, 1, A["q"], 10, 64, A["y"], None) == UNS
     assert g(0, 1, A["q"], -1, 64, A["y"], None) == INV
     assert g(0, 1, A["q"], 0, 64, A["y"], None) == 0   # empty: nothing to do
+
+
+def test_swa_validation_codes(lib):
+    """Sliding-window entry points: every invalid argument is refused on the
+    host before any launch (fake device addresses are never dereferenced)."""
+    INV, UNS = 1, 2
+    f = lib.linattn_swa_prefill
+
+    def pre(**kw):
+        a = dict(dtype=1, B=1, H=2, N=128, d=64, w=64, scale=0.125, q=A["q"], k=A["k"],
+                 v=A["v"], y=A["y"], kc=None, vc=None)
+        a.update(kw)
+        return f(a["dtype"], a["B"], a["H"], a["N"], a["d"], a["w"], a["scale"], a["q"],
+                 a["k"], a["v"], a["y"], a["kc"], a["vc"], None)
+
+    assert pre(q=None) == INV
+    assert pre(N=0) == INV
+    assert pre(w=0) == INV
+    assert pre(scale=float("nan")) == INV
+    assert pre(scale=float("inf")) == INV
+    assert pre(d=48) == UNS
+    assert pre(dtype=7) == INV
+    assert pre(kc=A["Si"]) == INV                     # v_cache missing
+    assert pre(y=A["k"]) == INV                       # output aliases an input
+    assert pre(kc=A["Si"], vc=A["Si"]) == INV         # the two caches overlap
+    assert pre(q=ctypes.c_void_p(0x10000004)) == INV  # misaligned
+    g = lib.linattn_swa_decode_step
+
+    def dec(**kw):
+        a = dict(dtype=1, B=2, H=2, d=64, w=64, scale=0.125, q=A["q"], k=A["k"], v=A["v"],
+                 pos=A["zi"], kc=A["Si"], vc=A["So"], y=A["y"])
+        a.update(kw)
+        return g(a["dtype"], a["B"], a["H"], a["d"], a["w"], a["scale"], a["q"], a["k"],
+                 a["v"], a["pos"], a["kc"], a["vc"], a["y"], None)
+
+    assert dec(pos=None) == INV
+    assert dec(kc=None) == INV
+    assert dec(w=4097) == UNS                         # beyond the generation window
+    assert dec(d=16) == UNS
+    assert dec(pos=ctypes.c_void_p(0x60000004)) == INV  # pos not 8-byte aligned
+    assert dec(y=A["Si"]) == INV                      # y aliases the key cache
+    assert dec(kc=A["q"]) == INV                      # cache aliases an input
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus 2 exits with status 2 and says why
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
