@@ -470,9 +470,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
-              "path (sequences and heads shard across GPUs with no exchange; "
-              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU "
+              "path (sequences and heads shard across GPUs with no exchange). "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

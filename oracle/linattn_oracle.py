@@ -26,7 +26,7 @@ Sources (page titles as printed; section in brackets):
 Everything here is plain float64 numpy.  The functions follow the
 definitions as written; there is no chunking, blocking or fusion.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * elu(x)+1 is named by the [TR] abstract's source paper but not defined on
     the pages: ELU with alpha = 1, so phi(x) = x + 1 for x > 0 and exp(x) for
     x <= 0 (both branches give 1 at 0).
