@@ -1050,43 +1050,73 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
 
 // Exclusive prefix over the summed parts, in place: slot s <- init +
 // sum_{p<s} T_p, where slot p+1 held part p's sum T_p and init is the
-// initial state (output segment s then reads slot s * sum_split).
-// Gated form: slot s <- 2^l_s slot(s-1) + T_(s-1), with l_s the log2 decay of
-// segment s - 1 (ws_log).  Used when there are too many segments per head for
-// each output workgroup to add up its predecessors' sums itself.
+// initial state (output segment s then reads slot s * sum_split).  Gated
+// form: slot s <- 2^l_s slot(s-1) + T_(s-1), with l_s the log2 decay of part
+// s - 1 (ws_log).  Used when there are too many parts per head for each
+// output workgroup to add up its predecessors itself.
+//
+// Two levels, so that the serial chain per element is a quarter of the
+// slots: a workgroup takes 64 float4 elements of one head's slots, and its
+// 4 waves split the slots 1 .. nscan-1 into 4 contiguous groups.  Each
+// thread forms its group's total (and the group's log2 decay), the group
+// totals meet in LDS, each thread combines the totals of the groups before
+// its own into the prefix entering its group, and then rewrites its group's
+// slots as running prefixes.
+constexpr int kScanCols = 64;    // float4 elements per workgroup
+constexpr int kScanGroups = 4;   // slot groups (one per wave)
+
 template <int MAP, int DK, int DV>
 __global__ __launch_bounds__(256) void seg_scan_kernel(PrefillArgs a) {
   using SS = StateShape<MAP, DK, DV>;
   constexpr int Q = SS::SLOT / 4;  // float4 per slot
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int bh = (int)(idx / Q);
-  if (bh >= a.BH) return;
-  const int e4 = (int)(idx % Q);
+  static_assert(Q % kScanCols == 0, "a slot is whole 64-element columns");
+  constexpr int TILES = Q / kScanCols;
+  __shared__ f32x4_t tot[kScanGroups][kScanCols];
+  __shared__ float ltot[kScanGroups];
+  const int bh = blockIdx.x / TILES;
+  const int col = threadIdx.x % kScanCols;
+  const int e4 = (blockIdx.x % TILES) * kScanCols + col;
+  const int grp = threadIdx.x / kScanCols;  // wave-uniform
+  const int nscan = (a.nseg - 1) * a.sum_split + 1;  // slot 0 and every sum
+  const int per = (nscan - 1 + kScanGroups - 1) / kScanGroups;
+  const int s_lo = 1 + grp * per;
+  const int s_hi = s_lo + per < nscan ? s_lo + per : nscan;
+  f32x4_t* p = reinterpret_cast<f32x4_t*>(a.ws + (size_t)bh * a.nslot * SS::SLOT) + e4;
+  const float* lg = a.ws_log != nullptr ? a.ws_log + (size_t)bh * a.nslot : nullptr;
+
+  // group total and the group's log2 decay
+  f32x4_t t = {0.0f, 0.0f, 0.0f, 0.0f};
+  float lsum = 0.0f;
+#pragma unroll 8
+  for (int s = s_lo; s < s_hi; ++s) {
+    const f32x4_t v = p[(size_t)s * Q];
+    if (lg != nullptr) {
+      t *= __builtin_amdgcn_exp2f(lg[s]);
+      lsum += lg[s];
+    }
+    t += v;
+  }
+  tot[grp][col] = t;
+  if (col == 0) ltot[grp] = lsum;
+  lds_barrier();
+
+  // the state entering this group: the initial state, then earlier groups
   f32x4_t run = {0.0f, 0.0f, 0.0f, 0.0f};
   if (a.S_in != nullptr) {
     const int rt = e4 / (SS::NCT * 64);
     const int ct = (e4 / 64) % SS::NCT;
-    run = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, a.sym != 0, bh, rt, ct,
-                                    e4 % 64);
+    run = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, a.sym != 0, bh, rt, ct, e4 % 64);
   }
-  f32x4_t* p = reinterpret_cast<f32x4_t*>(a.ws + (size_t)bh * a.nslot * SS::SLOT) + e4;
-  const float* lg = a.ws_log != nullptr ? a.ws_log + (size_t)bh * a.nslot : nullptr;
-  const int nscan = (a.nseg - 1) * a.sum_split + 1;  // slot 0 and every sum
-  p[0] = run;
-  // batches of 16 slots: all loads of a batch are in flight at once
-  constexpr int kB = 16;
-  for (int s0 = 1; s0 < nscan; s0 += kB) {
-    f32x4_t t[kB];
-#pragma unroll
-    for (int j = 0; j < kB; ++j)
-      if (s0 + j < nscan) t[j] = p[(size_t)(s0 + j) * Q];
-#pragma unroll
-    for (int j = 0; j < kB; ++j)
-      if (s0 + j < nscan) {
-        if (lg != nullptr) run *= __builtin_amdgcn_exp2f(lg[s0 + j]);
-        run += t[j];
-        p[(size_t)(s0 + j) * Q] = run;
-      }
+  for (int g = 0; g < grp; ++g) {
+    if (lg != nullptr) run *= __builtin_amdgcn_exp2f(ltot[g]);
+    run += tot[g][col];
+  }
+  if (grp == 0) p[0] = run;
+#pragma unroll 8
+  for (int s = s_lo; s < s_hi; ++s) {
+    if (lg != nullptr) run *= __builtin_amdgcn_exp2f(lg[s]);
+    run += p[(size_t)s * Q];
+    p[(size_t)s * Q] = run;
   }
 }
 
@@ -1098,9 +1128,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, false, GATED>),
                        dim3(a.BH * (a.nseg - 1) * a.sum_split), dim3(NT), 0, st, a);
     if (a.prefix_mode == 2) {
-      const int64_t threads = (int64_t)a.BH * (SS::SLOT / 4);
       hipLaunchKernelGGL((seg_scan_kernel<MAP, DK, DV>),
-                         dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                         dim3((unsigned)(a.BH * (SS::SLOT / 4 / kScanCols))), dim3(256), 0,
                          st, a);
     }
   }
