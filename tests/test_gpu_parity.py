@@ -114,12 +114,14 @@ def _qk_scale(fmap):
 @pytest.mark.parametrize("fmap,d_k,d_v", SHAPES)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("N,seg_len", [(1, 0), (63, 0), (65, 64), (200, 64),
-                                       (517, 128), (700, 0), (1100, 512), (3000, 512)])
+                                       (517, 128), (700, 0), (1000, 320), (1100, 512),
+                                       (3000, 512)])
 def test_prefill_small(fmap, d_k, d_v, dtype, N, seg_len):
-    """Every kernel shape against the oracle.  The last two cases split the
-    segment-sum pass in two (8-chunk segments): with 3 segments the output
-    workgroups add the 4 preceding part sums themselves, with 6 segments (10
-    parts) the scan kernel forms the prefixes."""
+    """Every kernel shape against the oracle, including 1- and 5-chunk
+    segments.  The last two cases split the Taylor segment-sum pass in two
+    (8-chunk segments): with 3 segments the output workgroups add the 4
+    preceding part sums themselves, with 6 segments (10 parts) the scan
+    kernel forms the prefixes."""
     _log(f"prefill {fmap} {d_k}x{d_v} {dtype} N={N} seg_len={seg_len}")
     scale = _qk_scale(fmap)
     q, k, v = synth.draw_qkv(2, 3, N, d_k, d_v, seed=N, dtype=dtype, qk_scale=scale)
