@@ -702,10 +702,14 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
     }
   };
 
-  // TAYLOR2 query of the current chunk as floats: qv[16] = q,
-  // qb8[t] = q[8 (g & 1) + t]
-  float qv[MAP == MAP_TAYLOR2 && OUT ? DK : 1];
-  float qb8[MAP == MAP_TAYLOR2 && OUT ? 8 : 1];
+  // TAYLOR2 query of the current chunk (lane: query i16 of the wave's tile,
+  // lane group g), prepared once per chunk: qa8[k] = q[2k + (g >> 1)] / 2
+  // and qb8[t] = q[8 (g & 1) + t] are the two factors of the pair features
+  // of block k < 8; q8f is the operand of block 8 (the constant, the linear
+  // features, zero pads).  Vector values, not arrays: an array indexed by a
+  // loop counter before unrolling can be placed in LDS by the compiler.
+  f32x8_t qa8 = {}, qb8 = {};
+  frag q8f = E::zero();
 
   // phi(K)^T operand for state row tile rt, key block jb2: lane (rho = i16,
   // g) slot t <-> feature 16 rt + rho, token 32 jb2 + 8 g + t.
@@ -766,20 +770,11 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
     if constexpr (MAP == MAP_ELU1) {
       return qf[b][kb < NKB ? kb : 0];
     } else {
+      if (kb >= 8) return q8f;
+      const float qa = qa8[kb];
       float f[8];
-      if (kb < 8) {
-        const float qa = 0.5f * ((g >> 1) ? qv[2 * kb + 1] : qv[2 * kb]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) f[t] = qa * qb8[t];
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float g0 = t == 0 ? 1.0f : qv[t > 0 ? t - 1 : 0];
-          const float g1 = qv[7 + t];
-          const float g2 = t == 0 ? qv[15] : 0.0f;
-          f[t] = g == 0 ? g0 : (g == 1 ? g1 : (g == 2 ? g2 : 0.0f));
-        }
-      }
+      for (int t = 0; t < 8; ++t) f[t] = qa * qb8[t];
       return E::make(f);
     }
   };
@@ -857,19 +852,26 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
     frag qraw = E::zero();
     if constexpr (OUT) if (qwave) {
       if constexpr (MAP == MAP_TAYLOR2) {
+        f32x16_t qx;
 #pragma unroll
         for (int u = 0; u < SH::NQU; ++u) {
           float part[EPU];
           unpack16<T>(qs[b][u], part);
 #pragma unroll
-          for (int e = 0; e < EPU; ++e) qv[u * EPU + e] = part[e];
+          for (int e = 0; e < EPU; ++e) qx[u * EPU + e] = part[e];
         }
+        float f[8], f8[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) qb8[t] = (g & 1) ? qv[8 + t] : qv[t];
-        float f[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) f[t] = g < 2 ? qb8[t] : 0.0f;
+        for (int t = 0; t < 8; ++t) {
+          qb8[t] = (g & 1) ? qx[8 + t] : qx[t];
+          qa8[t] = 0.5f * ((g >> 1) ? qx[2 * t + 1] : qx[2 * t]);
+          f[t] = g < 2 ? qb8[t] : 0.0f;
+          const float g0 = t == 0 ? 1.0f : qx[t > 0 ? t - 1 : 0];
+          const float g2 = t == 0 ? qx[15] : 0.0f;
+          f8[t] = g == 0 ? g0 : (g == 1 ? qx[7 + t] : (g == 2 ? g2 : 0.0f));
+        }
         qraw = E::make(f);
+        q8f = E::make(f8);
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) O[ct] = {0.0f, 0.0f, 0.0f, 0.0f};
