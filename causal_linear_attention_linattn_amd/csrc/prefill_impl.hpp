@@ -398,6 +398,18 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
   // waves that own one of the chunk's 4 query tiles (all of them when NW = 4)
   const bool qwave = NW == 4 || w < 4;
   const int lane = tid & 63;
+  // State row tile m of this wave (a tile index >= NRT means none).  The
+  // 8-wave output kernels give the output waves 0-3 two tiles each (w, w+4)
+  // and waves 4-7 the rest (8 + (w-4) + 4m), which evens out the per-wave
+  // matrix work; otherwise wave w owns tiles w, w + NW, ...
+  auto row_tile = [&](int m) __attribute__((always_inline)) -> int {
+    if constexpr (OUT && NW == 8) {
+      static_assert(SH::NRT <= 8 + 4 * SH::MAXRT, "tiles 8.. fit the waves 4-7");
+      return w < 4 ? (m < 2 ? w + 4 * m : SH::NRT + 64) : 8 + (w - 4) + 4 * m;
+    } else {
+      return w + NW * m;
+    }
+  };
   const int i16 = lane & 15;
   const int g = lane >> 4;
 
@@ -429,7 +441,7 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
   f32x4_t Sacc[SH::MAXRT][NCT];
 #pragma unroll
   for (int m = 0; m < SH::MAXRT; ++m) {
-    const int rt = w + NW * m;
+    const int rt = row_tile(m);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -470,7 +482,7 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
         fj = __builtin_amdgcn_exp2f(__uint_as_float(buffer_load4(rl, (uint32_t)j * 4u)));
 #pragma unroll
       for (int m = 0; m < SH::MAXRT; ++m) {
-        const int rt = w + NW * m;
+        const int rt = row_tile(m);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const uint32_t off = rt < NRT ? ((uint32_t)j * SH::SLOT + ((rt * NCT + ct) * 64 + lane) * 4) * 4u
@@ -783,7 +795,7 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
   auto publish_state = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < SH::MAXRT; ++m) {
-      const int rt = w + NW * m;
+      const int rt = row_tile(m);
       if (rt >= NRT) continue;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -946,7 +958,7 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
       // state update: S' += phi(K)^T V' for this wave's row tiles
 #pragma unroll
       for (int m = 0; m < SH::MAXRT; ++m) {
-        const int rt = w + NW * m;
+        const int rt = row_tile(m);
         if (rt >= NRT) continue;
         const frag ak = kt_frag(b, rt, jb2, u);
 #pragma unroll
@@ -1017,7 +1029,7 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
     const float n_pad = (float)(((nchunks + P - 1) / P) * P * C - ntok);
 #pragma unroll
     for (int m = 0; m < SH::MAXRT; ++m) {
-      const int rt = w + NW * m;
+      const int rt = row_tile(m);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int row = 16 * rt + 4 * g + t;
@@ -1032,7 +1044,7 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
     if (seg == a.nseg - 1 && a.S_out != nullptr) {
 #pragma unroll
       for (int m = 0; m < SH::MAXRT; ++m) {
-        const int rt = w + NW * m;
+        const int rt = row_tile(m);
         if (rt >= NRT) continue;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -1045,7 +1057,7 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
         a.ws + ((size_t)bh * a.nslot + seg + 1) * SH::SLOT);
 #pragma unroll
     for (int m = 0; m < SH::MAXRT; ++m) {
-      const int rt = w + NW * m;
+      const int rt = row_tile(m);
       if (rt >= NRT) continue;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) p[(rt * NCT + ct) * 64 + lane] = Sacc[m][ct];
