@@ -432,8 +432,8 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
   }
 }
 
-// Generation step for windows of at most kSwaSmallWindow slots (the pages
-// use 64 and at most 128).  Every cache row is loaded at entry through a
+// Generation step for windows of at most WM slots (WM = 64 or 128; the
+// pages use 64 and at most 128).  Every cache row is loaded at entry through a
 // buffer resource over the head's cache (rows past the window read as
 // zero; rows not yet filled are masked by selects, since they may hold
 // anything), together with the query and the new token, so the step waits
@@ -442,8 +442,9 @@ __global__ __launch_bounds__(256) void swa_decode_kernel(const T* __restrict__ q
 // scores in LDS with DPP wave reductions, and each thread exponentiates the
 // scores of its own value rows.  Value partials are summed through LDS.
 constexpr int kSwaSmallWindow = 128;
+constexpr int kSwaSmallThreads64 = 256;  // threads per head when the window is <= 64
 
-template <typename T, int D, int NTH>
+template <typename T, int D, int NTH, int WM>
 __global__ __launch_bounds__(NTH) void swa_decode_small_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int64_t* __restrict__ pos, T* __restrict__ kc, T* __restrict__ vc,
@@ -453,13 +454,14 @@ __global__ __launch_bounds__(NTH) void swa_decode_small_kernel(
   constexpr uint32_t ES = sizeof(T);
   constexpr int EPU = E::kPer16B;
   constexpr int UR = D / EPU;                       // 16-byte units per key row
-  constexpr int NK = kSwaSmallWindow * UR / NTH;    // key units per thread
+  constexpr int NK = WM * UR / NTH;                 // key units per thread
   constexpr int CPR = D / 4;                        // 4-column groups per row
   constexpr int VPP = NTH / CPR;                    // value rows per pass
-  constexpr int NV = kSwaSmallWindow / VPP;         // value groups per thread
+  constexpr int NV = WM / VPP;                      // value groups per thread
+  static_assert((WM == 64 || WM == 128) && WM <= kSwaSmallWindow, "window capacity");
   static_assert(NK >= 1 && NV >= 1 && NTH % UR == 0 && NTH % CPR == 0 && NTH >= D,
                 "tiling");
-  __shared__ float sp[kSwaSmallWindow];
+  __shared__ float sp[WM];
   __shared__ __align__(16) float red[VPP][D];
 
   const int bh = blockIdx.x;
@@ -533,11 +535,12 @@ __global__ __launch_bounds__(NTH) void swa_decode_small_kernel(
   }
   lds_barrier();
 
-  // softmax statistics, per wave (every slot index is below 128)
-  const float s0 = sp[lane], s1 = sp[lane + 64];
+  // softmax statistics, per wave (every slot index is below WM)
+  const float s0 = sp[lane], s1 = WM > 64 ? sp[(lane + 64) & (WM - 1)] : -1e30f;
   const float mx = wave_max(fmaxf(s0, s1));
   const float sum = wave_sum((lane < nvalid ? __builtin_amdgcn_exp2f(s0 - mx) : 0.0f) +
-                             (lane + 64 < nvalid ? __builtin_amdgcn_exp2f(s1 - mx) : 0.0f));
+                             (WM > 64 && lane + 64 < nvalid ? __builtin_amdgcn_exp2f(s1 - mx)
+                                                            : 0.0f));
 
   // ------------------------------------------------------------ values --
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -584,10 +587,18 @@ hipError_t launch_swa_decode(const void* q, const void* k, const void* v,
                              const int64_t* pos, void* kc, void* vc, void* y,
                              int64_t B, int64_t H, int64_t window, float scale,
                              hipStream_t st) {
+  if (window <= 64) {
+    constexpr int NTH = kSwaSmallThreads64;
+    hipLaunchKernelGGL((swa_decode_small_kernel<T, D, NTH, 64>), dim3((unsigned)(B * H)), dim3(NTH),
+                       0, st, reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k),
+                       reinterpret_cast<const T*>(v), pos, reinterpret_cast<T*>(kc),
+                       reinterpret_cast<T*>(vc), reinterpret_cast<T*>(y), (int)H, (int)window,
+                       scale * kLog2e);
+    return hipGetLastError();
+  }
   if (window <= kSwaSmallWindow) {
-    constexpr int NTH = 256;
-    hipLaunchKernelGGL((swa_decode_small_kernel<T, D, NTH>), dim3((unsigned)(B * H)), dim3(NTH), 0,
-                       st, reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k),
+    hipLaunchKernelGGL((swa_decode_small_kernel<T, D, 256, 128>), dim3((unsigned)(B * H)), dim3(256),
+                       0, st, reinterpret_cast<const T*>(q), reinterpret_cast<const T*>(k),
                        reinterpret_cast<const T*>(v), pos, reinterpret_cast<T*>(kc),
                        reinterpret_cast<T*>(vc), reinterpret_cast<T*>(y), (int)H, (int)window,
                        scale * kLog2e);
