@@ -336,13 +336,13 @@ def intra_mfma_probe(torch, iters=2000):
 # Sources that define the kernels behind each recorded traffic figure: the
 # host launch code, the shared device code and the kernels' own files.
 DIGEST_FILES = {
-    "prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp",
+    "prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp", "chunk_walk.inc",
                 "prefill_elu1_bf16.hip"),
     "decode": ("api.hip", "device.hpp", "shapes.hpp", "decode.hip"),
     "taylor2_prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp",
-                        "prefill_taylor2_bf16.hip"),
+                        "chunk_walk.inc", "prefill_taylor2_bf16.hip"),
     "gated_prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp",
-                      "prefill_elu1_bf16_gated.hip"),
+                      "chunk_walk.inc", "prefill_elu1_bf16_gated.hip"),
     "swa_prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp", "swa.hip"),
     "swa_decode": ("api.hip", "device.hpp", "shapes.hpp", "swa.hip"),
 }

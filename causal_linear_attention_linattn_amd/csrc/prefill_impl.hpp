@@ -398,18 +398,6 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
   // waves that own one of the chunk's 4 query tiles (all of them when NW = 4)
   const bool qwave = NW == 4 || w < 4;
   const int lane = tid & 63;
-  // State row tile m of this wave (a tile index >= NRT means none).  The
-  // 8-wave output kernels give the output waves 0-3 two tiles each (w, w+4)
-  // and waves 4-7 the rest (8 + (w-4) + 4m), which evens out the per-wave
-  // matrix work; otherwise wave w owns tiles w, w + NW, ...
-  auto row_tile = [&](int m) __attribute__((always_inline)) -> int {
-    if constexpr (OUT && NW == 8) {
-      static_assert(SH::NRT <= 8 + 4 * SH::MAXRT, "tiles 8.. fit the waves 4-7");
-      return w < 4 ? (m < 2 ? w + 4 * m : SH::NRT + 64) : 8 + (w - 4) + 4 * m;
-    } else {
-      return w + NW * m;
-    }
-  };
   const int i16 = lane & 15;
   const int g = lane >> 4;
 
@@ -437,634 +425,36 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
   const auto rg = make_rsrc(GATED ? a.gate + (size_t)bh * N + tok_begin : nullptr,
                             GATED ? (uint32_t)ntok * 4u : 0u);
 
-  // ------------------------------------------------------------ state ----
-  f32x4_t Sacc[SH::MAXRT][NCT];
-#pragma unroll
-  for (int m = 0; m < SH::MAXRT; ++m) {
-    const int rt = row_tile(m);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (OUT && rt < NRT) {
-        if (a.prefix_mode == 2) {
-          // scanned workspace: slot seg * sum_split holds the exclusive
-          // prefix of the segment
-          const f32x4_t* p = reinterpret_cast<const f32x4_t*>(
-              a.ws + ((size_t)bh * a.nslot + seg * a.sum_split) * SH::SLOT);
-          s = p[(rt * NCT + ct) * 64 + lane];
-        } else if (a.S_in != nullptr) {
-          s = state_in_tile<MAP, DK, DV>(a.S_in, a.z_in, a.sym != 0, bh, rt, ct,
-                                        lane);
-        }
-      }
-      Sacc[m][ct] = s;
-    }
-  }
-  if (OUT && a.prefix_mode == 1 && seg > 0) {
-    // Few segments: add the sums of the preceding segments (slots 1 .. seg)
-    // directly.  The loads go through a buffer resource that covers exactly
-    // those slots, so the fixed-trip loop below issues every load at once
-    // and the slots past `seg` read as zero.  (Rows past NRT, which exist
-    // only when NRT is not a multiple of the wave count, take an
-    // out-of-range offset; those accumulators are never used.)
-    // Gated: the state entering segment j + 1 is the one entering segment j
-    // scaled by segment j's total decay, plus segment j's own sum; the
-    // log2 decays past `seg` read as 0 (factor 1).
-    const int npre = seg * a.sum_split;  // sums of the parts before seg
-    const auto rw = make_rsrc(a.ws + ((size_t)bh * a.nslot + 1) * SH::SLOT,
-                              (uint32_t)npre * SH::SLOT * 4u);
-    const auto rl = make_rsrc(GATED ? a.ws_log + (size_t)bh * a.nslot + 1 : nullptr,
-                              GATED ? (uint32_t)npre * 4u : 0u);
-#pragma unroll
-    for (int j = 0; j < kDirectPrefixMax - 1; ++j) {
-      float fj = 1.0f;
-      if constexpr (GATED)
-        fj = __builtin_amdgcn_exp2f(__uint_as_float(buffer_load4(rl, (uint32_t)j * 4u)));
-#pragma unroll
-      for (int m = 0; m < SH::MAXRT; ++m) {
-        const int rt = row_tile(m);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const uint32_t off = rt < NRT ? ((uint32_t)j * SH::SLOT + ((rt * NCT + ct) * 64 + lane) * 4) * 4u
-                                        : kOOB;
-          const f32x4_t t = __builtin_bit_cast(f32x4_t, buffer_load16(rw, off));
-          if constexpr (GATED)
-            Sacc[m][ct] = Sacc[m][ct] * fj + t;
-          else
-            Sacc[m][ct] += t;
-        }
-      }
-    }
-  }
-
-  // ones column of V' (and ones row of V'^T): lane column 0 of the last tile
-  float onesv[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) onesv[t] = i16 == 0 ? 1.0f : 0.0f;
-  const frag ones = E::make(onesv);
-  // ------------------------------------------------- tile operand access --
-  using CT = ChunkTiles<MAP, T, DK, DV>;
-  auto v_frag = [&](int b, int jb2, int ct) __attribute__((always_inline)) -> frag {
-    return CT::v_frag(sV(b), jb2, ct, lane);
+  // ------------------------------------------------------------ roles ----
+  // The 8-wave output kernels run two specialised walks side by side: waves
+  // 0-3 make the chunk's outputs and own no state; waves 4-7 own every state
+  // row tile (tiles w-4, w, w+4, w+8 of the pair features, then the
+  // constant/linear tiles 16 and 17 on waves 4 and 5).  Each walk is
+  // straight-line code with registers of its own, and both pass the same
+  // barriers.  Other kernels run one walk in which every wave does both.
+  auto walk = [&](auto role_c) __attribute__((always_inline)) {
+    constexpr int ROLE = decltype(role_c)::value;  // 1: outputs, 2: state
+    const bool qwave_r = ROLE == 1;
+    constexpr int kMT = ROLE == 1 ? 1 : (SH::NRT + 3) / 4;
+    static_assert(MAP != MAP_ELU1 && SH::NRT == 18, "the split owns 16 + 2 tiles");
+    // state row tile m of this wave (a tile index >= NRT means none)
+    auto row_tile = [&](int m) __attribute__((always_inline)) -> int {
+      return ROLE == 1 ? SH::NRT + 64 : (w - 4) + 4 * m;
+    };
+#include "chunk_walk.inc"
   };
 
-  // ---------------------------------------------------------- staging ----
-  St st[P];
-
-  auto issue = [&](int c, St& s) __attribute__((always_inline)) {
-    const uint32_t cb = (uint32_t)c * C;  // first token of chunk c
-    if constexpr (BF) {
-#pragma unroll
-      for (int u = 0; u < St::NK; ++u) {
-        const int p = tid + u * SH::NT;
-        const uint32_t off = ((cb + p / RTK::UPR) * DK + (p % RTK::UPR) * 8) * ES;
-        s.k[u] = buffer_load16(rk, p < SH::UK ? off : kOOB);
-      }
-#pragma unroll
-      for (int u = 0; u < St::NV; ++u) {
-        const int p = tid + u * SH::NT;
-        const uint32_t off = ((cb + p / RTV::UPR) * DV + (p % RTV::UPR) * 8) * ES;
-        s.v[u] = buffer_load16(rv, p < SH::UV ? off : kOOB);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < SH::NPK; ++u) {
-        const int pu = tid + u * SH::NT;
-        const uint32_t r0 = cb + 2 * (pu / SH::KUR);
-        const uint32_t e0 = (pu % SH::KUR) * EPU;
-        const uint32_t off = pu < SH::PK ? (r0 * DK + e0) * ES : kOOB;
-        s.k[2 * u] = buffer_load16(rk, off);
-        s.k[2 * u + 1] = buffer_load16(rk, pu < SH::PK ? off + DK * ES : kOOB);
-      }
-#pragma unroll
-      for (int u = 0; u < SH::NPV; ++u) {
-        const int pu = tid + u * SH::NT;
-        const uint32_t r0 = cb + 2 * (pu / SH::VUR);
-        const uint32_t e0 = (pu % SH::VUR) * EPU;
-        const uint32_t off = pu < SH::PV ? (r0 * DV + e0) * ES : kOOB;
-        s.v[2 * u] = buffer_load16(rv, off);
-        s.v[2 * u + 1] = buffer_load16(rv, pu < SH::PV ? off + DV * ES : kOOB);
-      }
-    }
-    if constexpr (OUT) if (qwave) {
-      const uint32_t tq = cb + 16 * w + i16;
-      if constexpr (MAP == MAP_ELU1) {
-        constexpr int UPB = 8 / EPU;  // 16-byte units per 8-feature block
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int h = 0; h < UPB; ++h) {
-            const uint32_t f0 = 32 * kb + 8 * g + h * EPU;
-            s.q[kb * UPB + h] = buffer_load16(rq, f0 < DK ? (tq * DK + f0) * ES : kOOB);
-          }
-      } else {
-#pragma unroll
-        for (int u = 0; u < SH::NQU; ++u)
-          s.q[u] = buffer_load16(rq, (tq * DK + u * EPU) * ES);
-      }
-    }
-    if constexpr (GATED) {
-      if (w == 0) s.gt = __uint_as_float(buffer_load4(rg, (cb + lane) * 4u));
-    }
-  };
-
-  // Gated form: the decay of chunk `chunk` from its ring slot into copy b.
-  // Wave 0 takes log2 of each coefficient (tokens past the segment end get
-  // 0, i.e. a = 1, and never count as resets) and runs a segmented
-  // inclusive scan over the 64 tokens: a reset restarts the sum.
-  auto stage_gate = [&](const St& s, int b, int chunk) __attribute__((always_inline)) {
-    if constexpr (GATED) {
-      if (w != 0) return;
-      const bool valid = chunk * C + lane < ntok;
-      const float lg = __builtin_amdgcn_logf(s.gt);
-      const bool reset = valid && !(lg >= kResetLog2);
-      float G = valid && !reset ? lg : 0.0f;
-      int L = reset ? lane : -1;
-      // Inclusive scan of (G, L) under "a later reset wins, else add": steps
-      // of 1, 2, 4, 8 lanes inside each row of 16, then the row totals
-      // through lanes 15 and 31.  A lane without a source receives the
-      // identity (0, -1).
-      auto combine = [&](auto ctrl, auto rows) __attribute__((always_inline)) {
-        constexpr int CTRL = decltype(ctrl)::value, ROWS = decltype(rows)::value;
-        const float Gp = __int_as_float(dpp_move<CTRL, ROWS>(0, __float_as_int(G)));
-        const int Lp = dpp_move<CTRL, ROWS>(-1, L);
-        if (L < 0) {
-          G += Gp;
-          L = Lp;
-        }
-      };
-      combine(std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xf>{});
-      combine(std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xf>{});
-      combine(std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xf>{});
-      combine(std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{});
-      combine(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{});
-      combine(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{});
-
-      const float Gend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), C - 1));
-      const int Lend = __builtin_amdgcn_readlane(L, C - 1);
-      sG[b][lane] = G;
-      sL[b][lane] = L;
-      sF[b][lane] = L >= 0 ? 0.0f : __builtin_amdgcn_exp2f(G);
-      sU[b][lane] = valid && lane >= Lend ? __builtin_amdgcn_exp2f(Gend - G) : 0.0f;
-    }
-  };
-
-  // Stage a chunk from its ring slot into LDS copy b.
-  auto write_tiles = [&](const St& s, int b) __attribute__((always_inline)) {
-    if constexpr (BF) {
-#pragma unroll
-      for (int u = 0; u < St::NK; ++u) {
-        const int p = tid + u * SH::NT;
-        if (SH::UK % SH::NT == 0 || p < SH::UK) {  // compile-time when tiles divide evenly
-          const int row = p / RTK::UPR, unit = p % RTK::UPR;
-          if constexpr (MAP == MAP_ELU1) {
-            float f[8];
-            unpack16<T>(s.k[u], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = phi_elu1(f[e]);
-            *reinterpret_cast<uint4*>(sK(b) + RTK::off(row, unit)) = pack16<T>(f);
-          } else {
-            if constexpr (OUT) *reinterpret_cast<uint4*>(sK(b) + RTK::off(row, unit)) = s.k[u];
-            const uint32_t wd[4] = {s.k[u].x, s.k[u].y, s.k[u].z, s.k[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              sKT(b)[(unit * 8 + 2 * e) * CS + row] = (bf16_t)(wd[e] & 0xffffu);
-              sKT(b)[(unit * 8 + 2 * e + 1) * CS + row] = (bf16_t)(wd[e] >> 16);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < St::NV; ++u) {
-        const int p = tid + u * SH::NT;
-        if (SH::UV % SH::NT == 0 || p < SH::UV)
-          *reinterpret_cast<uint4*>(sV(b) + RTV::off(p / RTV::UPR, p % RTV::UPR)) = s.v[u];
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < SH::NPK; ++u) {
-        const int pu = tid + u * SH::NT;
-        if (SH::PK % SH::NT == 0 || pu < SH::PK) {
-          const int r0 = 2 * (pu / SH::KUR);
-          const int e0 = (pu % SH::KUR) * EPU;
-          float f0[EPU], f1[EPU];
-          unpack16<T>(s.k[2 * u], f0);
-          unpack16<T>(s.k[2 * u + 1], f1);
-          if constexpr (MAP == MAP_ELU1) {
-#pragma unroll
-            for (int e = 0; e < EPU; ++e) {
-              f0[e] = phi_elu1(f0[e]);
-              f1[e] = phi_elu1(f1[e]);
-            }
-          }
-          if constexpr (OUT) {
-            *reinterpret_cast<uint4*>(sK(b) + r0 * KS + e0) = pack16<T>(f0);
-            *reinterpret_cast<uint4*>(sK(b) + (r0 + 1) * KS + e0) = pack16<T>(f1);
-          }
-#pragma unroll
-          for (int e = 0; e < EPU; ++e) store_pair(sKT(b) + (e0 + e) * CS + r0, f0[e], f1[e]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < SH::NPV; ++u) {
-        const int pu = tid + u * SH::NT;
-        if (SH::PV % SH::NT == 0 || pu < SH::PV) {
-          const int r0 = 2 * (pu / SH::VUR);
-          const int e0 = (pu % SH::VUR) * EPU;
-          float f0[EPU], f1[EPU];
-          unpack16<T>(s.v[2 * u], f0);
-          unpack16<T>(s.v[2 * u + 1], f1);
-#pragma unroll
-          for (int e = 0; e < EPU; ++e) store_pair(sV(b) + (e0 + e) * CS + r0, f0[e], f1[e]);
-        }
-      }
-    }
-  };
-
-  // Query operands, one set per LDS copy (the set of chunk c + 1 is formed
-  // while chunk c is computed).
-  //   ELU1:    qf[b][kb] = phi(q) over features 32kb + 8g + (0..7)
-  //   TAYLOR2: qs[b][u]  = the raw 16-byte units of q (expanded at use)
-  frag qf[2][MAP == MAP_ELU1 && OUT ? NKB : 1];
-  uint4 qs[2][MAP == MAP_TAYLOR2 && OUT ? SH::NQU : 1];
-
-  auto take_q = [&](const St& s, int b) __attribute__((always_inline)) {
-    if constexpr (!OUT) return;
-    if (!qwave) return;
-    if constexpr (MAP == MAP_ELU1) {
-      constexpr int UPB = 8 / EPU;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        float f[8];
-#pragma unroll
-        for (int h = 0; h < UPB; ++h) {
-          float part[EPU];
-          unpack16<T>(s.q[kb * UPB + h], part);
-#pragma unroll
-          for (int e = 0; e < EPU; ++e) f[h * EPU + e] = part[e];
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          f[t] = (32 * kb + 8 * g + t < DK) ? phi_elu1(f[t]) : 0.0f;
-        qf[b][kb] = E::make(f);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < SH::NQU; ++u) qs[b][u] = s.q[u];
-    }
-  };
-
-  // TAYLOR2 query of the current chunk (lane: query i16 of the wave's tile,
-  // lane group g), prepared once per chunk: qa8[k] = q[2k + (g >> 1)] / 2
-  // and qb8[t] = q[8 (g & 1) + t] are the two factors of the pair features
-  // of block k < 8; q8f is the operand of block 8 (the constant, the linear
-  // features, zero pads).  Vector values, not arrays: an array indexed by a
-  // loop counter before unrolling can be placed in LDS by the compiler.
-  f32x8_t qa8 = {}, qb8 = {};
-  frag q8f = E::zero();
-
-  // phi(K)^T operand for state row tile rt, key block jb2: lane (rho = i16,
-  // g) slot t <-> feature 16 rt + rho, token 32 jb2 + 8 g + t.
-  // GATED: slot t is scaled by u[t], the decay from its token to the chunk
-  // end.
-  auto kt_frag = [&](int b, int rt, int jb2, const float (&u)[8]) __attribute__((always_inline)) -> frag {
-    const int col = 32 * jb2 + 8 * g;
-    if constexpr (MAP == MAP_ELU1) {
-      if (16 * rt >= DK) return E::zero();
-      frag r;
-      if constexpr (BF)
-        r = CT::template tokfrag_bf<RTK>(sK(b), col, 16 * rt, lane);
-      else
-        r = E::load8(sKT(b) + (16 * rt + i16) * CS + col);
-      if constexpr (GATED) {
-        float f[8];
-        if constexpr (BF) {
-          unpack16<T>(__builtin_bit_cast(uint4, r), f);
-        } else {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) f[t] = r[t];
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) f[t] *= u[t];
-        r = E::make(f);
-      }
-      return r;
-    } else {
-      float f[8];
-      if (rt < 16) {
-        float fa[8], fb[8];
-        E::load8f(sKT(b) + rt * CS + col, fa);
-        E::load8f(sKT(b) + i16 * CS + col, fb);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) f[t] = fa[t] * fb[t];
-      } else if (rt == 16) {
-        float fb[8];
-        E::load8f(sKT(b) + (i16 == 0 ? 0 : i16 - 1) * CS + col, fb);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) f[t] = i16 == 0 ? 1.0f : fb[t];
-      } else {
-        float fb[8];
-        E::load8f(sKT(b) + 15 * CS + col, fb);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) f[t] = i16 == 0 ? fb[t] : 0.0f;
-      }
-      if constexpr (GATED) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) f[t] *= u[t];
-      }
-      return E::make(f);
-    }
-  };
-
-  // phi(Q) operand for feature block kb: lane (query i16, g) slot t <->
-  // feature 32 kb + 8 g + t.
-  auto q_frag = [&](int b, int kb) __attribute__((always_inline)) -> frag {
-    if constexpr (MAP == MAP_ELU1) {
-      return qf[b][kb < NKB ? kb : 0];
-    } else {
-      if (kb >= 8) return q8f;
-      const float qa = qa8[kb];
-      float f[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) f[t] = qa * qb8[t];
-      return E::make(f);
-    }
-  };
-
-  // Write this wave's state tiles into LDS copy b (column-major S'^T).
-  auto publish_state = [&](int b) __attribute__((always_inline)) {
-#pragma unroll
-    for (int m = 0; m < SH::MAXRT; ++m) {
-      const int rt = row_tile(m);
-      if (rt >= NRT) continue;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        T* p = sS(b) + (16 * ct + i16) * PS + 16 * rt + 4 * g;
-        const f32x4_t s = Sacc[m][ct];
-        if constexpr (BF) {
-          *reinterpret_cast<uint2*>(p) =
-              make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
-        } else {
-          *reinterpret_cast<float4*>(p) = make_float4(s[0], s[1], s[2], s[3]);
-        }
-      }
-    }
-  };
-
-  // Causal mask of the within-chunk scores (the same for every chunk): lane
-  // (key slot 4h + t of block jb2, query il) keeps the score iff the key
-  // 32 jb2 + 8 g + 4 h + t is not after the query.
-  const int il = 16 * w + i16;
-  bool keep[2][8];
-#pragma unroll
-  for (int jb2 = 0; jb2 < 2; ++jb2)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) keep[jb2][e] = 32 * jb2 + 8 * g + e <= il;
-
-  // Gated segment-sum pass: log2 of the segment's total decay (-inf once a
-  // reset has been passed).
-  float seg_log = 0.0f;
-
-  // One chunk, computed from LDS copy b and query set b: stage chunk c + 1
-  // from ring slot `nx` into copy 1 - b, refill the slot with chunk c + P,
-  // then the outputs (OUT) and the state update of chunk c.
-  auto iteration = [&](int c, St& nx, auto bc) __attribute__((always_inline)) {
-    constexpr int b = decltype(bc)::value;
-    const int cb = c * C;
-
-    write_tiles(nx, 1 - b);
-    take_q(nx, 1 - b);
-    stage_gate(nx, 1 - b, c + 1);
-    issue(c + 1 + P, nx);
-
-    // Gated form: decays of this chunk.  Query il carries the state from
-    // before the chunk with factor fq (0 past a reset); the chunk as a whole
-    // scales the carried state by fc.
-    float Gq = 0.0f, fq = 1.0f, fc = 1.0f;
-    int Lq = -1;
-    if constexpr (GATED) {
-      // chunk-end values are the same for every lane: keep them scalar
-      fc = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                                         __builtin_bit_cast(int, sF[b][C - 1])));
-      if constexpr (OUT) {
-        if (qwave) {
-          Gq = sG[b][il];
-          Lq = sL[b][il];
-          fq = sF[b][il];
-        }
-      } else {
-        const float Ge = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                                                       __builtin_bit_cast(int, sG[b][C - 1])));
-        const int Le = __builtin_amdgcn_readfirstlane(sL[b][C - 1]);
-        seg_log = Le >= 0 ? -__builtin_inff() : seg_log + Ge;
-      }
-    }
-
-    f32x4_t O[OUT ? NCT : 1];
-    frag qraw = E::zero();
-    if constexpr (OUT) if (qwave) {
-      if constexpr (MAP == MAP_TAYLOR2) {
-        f32x16_t qx;
-#pragma unroll
-        for (int u = 0; u < SH::NQU; ++u) {
-          float part[EPU];
-          unpack16<T>(qs[b][u], part);
-#pragma unroll
-          for (int e = 0; e < EPU; ++e) qx[u * EPU + e] = part[e];
-        }
-        float f[8], f8[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          qb8[t] = (g & 1) ? qx[8 + t] : qx[t];
-          qa8[t] = 0.5f * ((g >> 1) ? qx[2 * t + 1] : qx[2 * t]);
-          f[t] = g < 2 ? qb8[t] : 0.0f;
-          const float g0 = t == 0 ? 1.0f : qx[t > 0 ? t - 1 : 0];
-          const float g2 = t == 0 ? qx[15] : 0.0f;
-          f8[t] = g == 0 ? g0 : (g == 1 ? qx[7 + t] : (g == 2 ? g2 : 0.0f));
-        }
-        qraw = E::make(f);
-        q8f = E::make(f8);
-      }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) O[ct] = {0.0f, 0.0f, 0.0f, 0.0f};
-
-      // prefix term: O^T += S'^T phi(Q)^T
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const frag bq = q_frag(b, kb);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const frag av = E::load8(sS(b) + (16 * ct + i16) * PS + 32 * kb + 8 * g);
-          E::mma(O[ct], av, bq);
-        }
-      }
-      if constexpr (GATED) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) O[ct] *= fq;
-      }
-    }
-    if constexpr (GATED) {
-#pragma unroll
-      for (int m = 0; m < SH::MAXRT; ++m)
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) Sacc[m][ct] *= fc;
-    }
-
-    // Scheduling hint: interleave the staging arithmetic of chunk c + 1 (phi
-    // of k and q, independent of this chunk's products) with this chunk's
-    // first MFMAs, eight VALU instructions after each MFMA, so that the
-    // matrix unit is not idle while the wave computes phi.  Measured on the
-    // ELU1 shapes only; the TAYLOR2 schedule is left to the compiler.
-    if constexpr (MAP == MAP_ELU1) {
-      constexpr int kInterleave = OUT ? NKB * NCT : SH::MAXRT * NCT * 2;
-#pragma unroll
-      for (int i = 0; i < kInterleave; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // eight VALU
-      }
-    }
-
-    // Per 32-token key block: the V' operands serve both the within-chunk
-    // product (A-operand, V'^T) and the state update (B-operand, V').
-#pragma unroll
-    for (int jb2 = 0; jb2 < 2; ++jb2) {
-      frag vf[NCT - 1];
-#pragma unroll
-      for (int ct = 0; ct < NCT - 1; ++ct) vf[ct] = v_frag(b, jb2, ct);
-
-      // Gated form: weight u of key 32 jb2 + 8 g + e at the chunk end (zero
-      // across a reset, and past the segment end so that those tokens add
-      // nothing to the state).
-      float u[8];
-      if constexpr (GATED) {
-        const float4 u0 = *reinterpret_cast<const float4*>(&sU[b][32 * jb2 + 8 * g]);
-        const float4 u1 = *reinterpret_cast<const float4*>(&sU[b][32 * jb2 + 8 * g + 4]);
-        u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w;
-        u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
-      }
-
-      if constexpr (OUT) if (qwave) {
-        // within-chunk term: scores^T of this key block against the wave's
-        // queries (key blocks wholly after them come out fully masked)
-        frag bq[SH::NKBS];
-#pragma unroll
-        for (int kbs = 0; kbs < SH::NKBS; ++kbs) {
-          if constexpr (MAP == MAP_ELU1) bq[kbs] = q_frag(b, kbs); else bq[kbs] = qraw;
-        }
-        CT::template within_chunk<GATED>(sK(b), vf, bq, keep[jb2], ones, O, jb2, lane,
-                                         GATED ? &sG[b][32 * jb2 + 8 * g] : nullptr, Gq, Lq);
-      }
-
-      // state update: S' += phi(K)^T V' for this wave's row tiles
-#pragma unroll
-      for (int m = 0; m < SH::MAXRT; ++m) {
-        const int rt = row_tile(m);
-        if (rt >= NRT) continue;
-        const frag ak = kt_frag(b, rt, jb2, u);
-#pragma unroll
-        for (int ct = 0; ct < NCT - 1; ++ct) E::mma(Sacc[m][ct], ak, vf[ct]);
-        E::mma(Sacc[m][NCT - 1], ak, ones);
-      }
-    }
-
-    if constexpr (OUT) if (qwave) {
-      // normalise and write y (query il of this chunk; rows past the
-      // segment end fall outside the store range)
-      const float den = __shfl(O[NCT - 1][0], i16, 64);
-      const float rden = GATED && !a.normalize ? 1.0f : fast_rcp(den);
-      const uint32_t yrow = ((uint32_t)(cb + il) * DV + 4 * g) * ES;
-#pragma unroll
-      for (int ct = 0; ct < NCT - 1; ++ct) {
-        const f32x4_t o = O[ct];
-        const uint32_t off = yrow + 16 * ct * ES;
-        if constexpr (BF) {
-          const uint2 d = make_uint2(pack_bf16x2(o[0] * rden, o[1] * rden),
-                                     pack_bf16x2(o[2] * rden, o[3] * rden));
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, d), ry, off, 0, 0);
-        } else {
-          const uint4 d = make_uint4(__float_as_uint(o[0] * rden), __float_as_uint(o[1] * rden),
-                                     __float_as_uint(o[2] * rden), __float_as_uint(o[3] * rden));
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, d), ry, off, 0, 0);
-        }
-      }
-    }
-    if constexpr (OUT) {
-      // state through chunk c for the prefix term of chunk c + 1
-      if constexpr (NSB == 1) lds_barrier();  // every wave is done with sS
-      publish_state(1 - b);
-    }
-    lds_barrier();
-  };
-
-  // ------------------------------------------------------------ prologue --
-#pragma unroll
-  for (int s = 0; s < P; ++s) issue(s, st[s]);
-  if constexpr (OUT) publish_state(0);
-  write_tiles(st[0], 0);
-  take_q(st[0], 0);
-  stage_gate(st[0], 0, 0);
-  issue(P, st[0]);
-  lds_barrier();
-
-  // Chunk c is staged from ring slot c % P into LDS copy c % 2; one trip of
-  // P chunks keeps every ring index and copy index a compile-time constant.
-  // The loop runs whole trips with no branch between the copies; chunks
-  // past the segment end are inert (their loads are out of range and read
-  // zeros, their ones column is masked, and no y row of theirs is in the
-  // store range), so at most P - 1 empty chunks are walked at the end.
-  for (int c0 = 0; c0 < nchunks; c0 += P) {
-    static_for<0, P>([&](auto s) __attribute__((always_inline)) {
-      constexpr int S = decltype(s)::value;
-      iteration(c0 + S, st[(S + 1) % P], std::integral_constant<int, S % 2>{});
-    });
-  }
-
-  // Every token walked past the segment end (the tail of the last chunk and
-  // the empty chunks of the last trip) read k = 0 and v = 0: it added
-  // nothing to the value columns and phi(0) to the z column.  Take that
-  // back: phi(0) is 1 in every ELU1 feature, and in the TAYLOR2 constant
-  // feature (internal row 256) only.  (The gated form gives those tokens
-  // weight 0 instead, so that a strongly decayed z is not left to cancel.)
-  if constexpr (!GATED) {
-    const float n_pad = (float)(((nchunks + P - 1) / P) * P * C - ntok);
-#pragma unroll
-    for (int m = 0; m < SH::MAXRT; ++m) {
-      const int rt = row_tile(m);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int row = 16 * rt + 4 * g + t;
-        const bool unit_feature = MAP == MAP_ELU1 ? row < DK : row == 256;
-        if (i16 == 0 && unit_feature) Sacc[m][NCT - 1][t] -= n_pad;
-      }
-    }
-  }
-
-  // ------------------------------------------------------------ epilogue --
-  if constexpr (OUT) {
-    if (seg == a.nseg - 1 && a.S_out != nullptr) {
-#pragma unroll
-      for (int m = 0; m < SH::MAXRT; ++m) {
-        const int rt = row_tile(m);
-        if (rt >= NRT) continue;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          state_out_tile<MAP, DK, DV>(a.S_out, a.z_out, a.sym != 0, bh, rt,
-                                      ct, lane, Sacc[m][ct]);
-      }
-    }
+  if constexpr (OUT && NW == 8) {
+    if (w < 4)
+      walk(std::integral_constant<int, 1>{});
+    else
+      walk(std::integral_constant<int, 2>{});
   } else {
-    f32x4_t* p = reinterpret_cast<f32x4_t*>(
-        a.ws + ((size_t)bh * a.nslot + seg + 1) * SH::SLOT);
-#pragma unroll
-    for (int m = 0; m < SH::MAXRT; ++m) {
-      const int rt = row_tile(m);
-      if (rt >= NRT) continue;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) p[(rt * NCT + ct) * 64 + lane] = Sacc[m][ct];
-    }
-    if constexpr (GATED) {
-      if (tid == 0) a.ws_log[(size_t)bh * a.nslot + seg + 1] = seg_log;
-    }
+    constexpr int ROLE = 0;  // every wave: outputs (if any) and state
+    const bool qwave_r = qwave;
+    constexpr int kMT = SH::MAXRT;
+    auto row_tile = [&](int m) __attribute__((always_inline)) -> int { return w + NW * m; };
+#include "chunk_walk.inc"
   }
 }
 
