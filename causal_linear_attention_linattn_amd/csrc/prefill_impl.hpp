@@ -44,12 +44,15 @@
 namespace linattn {
 
 // Waves per chunk workgroup.  The Taylor state (18 row tiles) is spread
-// over 8 waves for bf16 inputs without decay, so that each holds fewer
-// accumulators and two waves share a SIMD (measured on one MI355X at
-// B=8 H=16 N=2048: 111.7 -> 106.6 us per call); with the decay factors or
-// float tiles the 8-wave build spills (gated: 130 -> 150 us), so those keep 4.
+// over 8 waves for bf16 inputs, so that each holds fewer accumulators and
+// two waves share a SIMD; in the output kernels waves 0-3 then make the
+// outputs and waves 4-7 own the state (the role split below).  Measured on
+// one MI355X at B=8 H=16 N=2048: 111.7 -> 106.6 us per call with every wave
+// doing both, 79.8 -> 70.7 us from the role split, and for the gated form
+// 107.2 -> 83.6 us (4 waves -> 8 split; 8 waves without the split spilled).
+// Float tiles keep 4 waves.
 template <int MAP, typename T, bool GATED>
-constexpr int kChunkWaves = MAP != MAP_ELU1 && sizeof(T) == 2 && !GATED ? 8 : 4;
+constexpr int kChunkWaves = MAP != MAP_ELU1 && sizeof(T) == 2 ? 8 : 4;
 
 template <int MAP, typename T, int DK, int DV, int NWAVES = 4>
 struct PrefillShape : StateShape<MAP, DK, DV> {
