@@ -285,6 +285,66 @@ def test_decode_graph_replays_match_eager(fmap, d_k, d_v):
         assert torch.equal(S_g, S_e) and torch.equal(z_g, z_e), r
 
 
+@pytest.mark.parametrize("case", ["one_segment", "part_sums", "scan", "taylor_state", "gated",
+                                  "sliding_window"])
+def test_prefill_graph_replays_match_eager(case):
+    """Prefill calls captured in one HIP graph: every replay (other eager work
+    in between) gives bit-identical outputs and final states to the same
+    calls run eagerly.  The cases cover one segment per head, output
+    workgroups adding their predecessors' part sums, the scan kernel, the
+    Taylor state export, the gated form, and the sliding-window prefill with
+    a generation step (its caches restored by an eager copy before each
+    replay)."""
+    _log(f"prefill graph replays {case}")
+    fmap, d_k, d_v, N, seg = {"one_segment": ("elu1", 64, 64, 300, 0),
+                              "part_sums": ("elu1", 64, 64, 1000, 192),
+                              "scan": ("elu1", 64, 64, 1000, 64),
+                              "taylor_state": ("taylor2", 16, 64, 700, 64),
+                              "gated": ("elu1", 64, 64, 1000, 64),
+                              "sliding_window": ("elu1", 64, 64, 700, 0)}[case]
+    q, k, v = synth.draw_qkv(2, 3, N, d_k, d_v, seed=41, dtype="bf16", qk_scale=_qk_scale(fmap))
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    ad = _gate_dev(synth.draw_gate(2, 3, N, seed=41, reset_p=0.01))
+    w = 64
+    qs, ks, vs = (ops.to_device(x, DEV)[:, :, 0].contiguous()
+                  for x in synth.draw_qkv(2, 3, 1, d_k, d_v, seed=41, dtype="bf16", stream=1))
+    pos = torch.full((2,), N, dtype=torch.int64, device=DEV)
+
+    def run(caches=None):
+        if case == "sliding_window":
+            y, (kc, vc) = ops.swa_prefill(qd, kd, vd, w, return_cache=True)
+            kc2, vc2 = caches if caches is not None else (kc, vc)
+            yd = ops.swa_decode_step(qs, ks, vs, pos, kc2, vc2, w)
+            return [y, yd, kc2, vc2]
+        if case == "gated":
+            y, (S, z) = ops.prefill_gated(qd, kd, vd, ad, fmap, return_state=True, seg_len=seg)
+            return [y, S, z]
+        y, (S, z) = ops.prefill(qd, kd, vd, fmap, return_state=True, seg_len=seg)
+        return [y, S, z]
+
+    if case == "sliding_window":
+        _, (kc0, vc0) = ops.swa_prefill(qd, kd, vd, w, return_cache=True)
+        kc_g, vc_g = kc0.clone(), vc0.clone()
+        eager = run((kc0.clone(), vc0.clone()))
+    else:
+        eager = run()
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        captured = run((kc_g, vc_g)) if case == "sliding_window" else run()
+    for r in range(3):
+        if case == "sliding_window":
+            kc_g.copy_(kc0)
+            vc_g.copy_(vc0)
+        junk = (vd.float() * 2.0).sum()  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for i, (a, b) in enumerate(zip(captured, eager)):
+            assert torch.equal(a, b), (r, i)
+
+
 # ------------------------------------------------------- gated form ------
 def _gate_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
