@@ -335,6 +335,18 @@ struct Stage {
   float gt;  // gated form: decay coefficient of token (lane) of the chunk
 };
 
+// An empty asm statement that takes each argument as read and written: the
+// compiler must assume new values, so nothing derived from them before this
+// point is reused after it.  Only when ON.
+template <class A>
+__device__ __forceinline__ void opaque1(A& a) {
+  asm volatile("" : "+v"(a));
+}
+template <bool ON, class... A>
+__device__ __forceinline__ void opaque_if(A&... a) {
+  if constexpr (ON) (opaque1(a), ...);
+}
+
 template <int I, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
@@ -444,7 +456,12 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
     auto row_tile = [&](int m) __attribute__((always_inline)) -> int {
       return ROLE == 1 ? SH::NRT + 64 : (w - 4) + 4 * m;
     };
+    const int tid_o = tid, lane_o = lane, i16_o = i16, g_o = g;
+    {
+      // mutable copies of the lane indices (see opaque_if in the walk)
+      int tid = tid_o, lane = lane_o, i16 = i16_o, g = g_o;
 #include "chunk_walk.inc"
+    }
   };
 
   if constexpr (OUT && NW == 8) {
