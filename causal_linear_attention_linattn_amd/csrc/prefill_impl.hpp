@@ -15,15 +15,18 @@
 // state-size count).  Every product is an MFMA (bf16 x bf16 -> fp32, or the
 // fp32 MFMA for float inputs); the state S' stays in fp32 accumulators.
 //
-// Parallel layout.  A workgroup of 4 waves owns one (batch*head, segment):
+// Parallel layout.  A workgroup of NW waves owns one (batch*head, segment):
 // a run of consecutive chunks walked in order.  Waves 0..3 produce the
-// outputs of the chunk's 16-token tiles (all value columns); every wave w of
-// the NW owns state row tiles w, w+NW, w+2NW, ... (16 features each) across
-// all columns.  NW = 4, or 8 for the bf16 Taylor state (kChunkWaves).  A bf16 (or
-// fp32) copy of S' in LDS, laid out column-major, feeds the inter term of
-// every wave.  K, V tiles are staged through LDS transposed (feature- and
-// value-major) so that every MFMA operand is one 16-byte LDS read; the next
-// chunk's global loads are issued before the current chunk is computed.
+// outputs of the chunk's 16-token tiles (all value columns).  With NW = 4
+// every wave w also owns state row tiles w, w+4, ... (16 features each)
+// across all columns.  The bf16 Taylor kernels have NW = 8 (kChunkWaves);
+// in their output kernels waves 4..7 own every state row tile and waves
+// 0..3 none (the role split below), and in their segment-sum kernels wave w
+// owns tiles w, w+8, ....  A bf16 (or fp32) copy of S' in LDS, laid out
+// column-major, feeds the inter term of every output wave.  K, V tiles are
+// staged through LDS (bf16 row-major, read transposed; fp32 transposed) so
+// that every MFMA operand is one or two LDS reads; the next chunks' global
+// loads are issued before the current chunk is computed.
 //
 // Several segments per head: chunk_kernel<OUT = false> sums each segment's
 // state, seg_scan_kernel turns those sums into exclusive prefixes (plus the
