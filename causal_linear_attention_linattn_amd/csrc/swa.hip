@@ -81,9 +81,11 @@ struct SwaTile {
     }
   }
 
+  // block kb < 0 (before the sequence) reads zeros
   __device__ static __forceinline__ void issue(__amdgpu_buffer_rsrc_t rk,
                                                __amdgpu_buffer_rsrc_t rv, int64_t kb,
                                                int tid, Stage& st) {
+    const bool before = kb < 0;
     const uint32_t rb = (uint32_t)(kb * C);  // first key row of the block
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -91,7 +93,8 @@ struct SwaTile {
       const int row = NR * (p / UR), e0 = (p % UR) * EPU;
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const uint32_t off = NU % 256 == 0 || p < NU ? ((rb + row + r) * D + e0) * ES : kOOB;
+        const uint32_t off = !before && (NU % 256 == 0 || p < NU) ? ((rb + row + r) * D + e0) * ES
+                                                                  : kOOB;
         st.k[u][r] = buffer_load16(rk, off);
         st.v[u][r] = buffer_load16(rv, off);
       }
@@ -141,7 +144,7 @@ struct SwaTile {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int64_t key = kb * C + 32 * jb2 + 8 * g + e;
-        const bool valid = key <= qi && key > qi - window;
+        const bool valid = key >= 0 && key <= qi && key > qi - window;
         s2[jb2][e] = valid ? sc[e >> 2][e & 3] * c : kNone;
         bmax = fmaxf(bmax, s2[jb2][e]);
       }
@@ -213,8 +216,10 @@ __global__ __launch_bounds__(256) void swa_prefill_kernel(const T* __restrict__ 
                                                           float c) {
   using TT = SwaTile<T, D>;
   constexpr int C = TT::C;
-  __shared__ __align__(16) T sK[TT::K_EL];
-  __shared__ __align__(16) T sV[TT::V_EL];
+  // bf16: a second copy of the block tiles for the two-block walk below
+  constexpr int NBUF = TT::BF ? 2 : 1;
+  __shared__ __align__(16) T sK[NBUF][TT::K_EL];
+  __shared__ __align__(16) T sV[NBUF][TT::V_EL];
 
   const int id = xcd_local_order(blockIdx.x, gridDim.x);
   const int bh = id / ntiles;
@@ -241,14 +246,28 @@ __global__ __launch_bounds__(256) void swa_prefill_kernel(const T* __restrict__ 
   float m = TT::kNone;
 
   typename TT::Stage st;
-  const int64_t klo = i0 - window + 1 > 0 ? i0 - window + 1 : 0;
-  TT::issue(rk, rv, klo / C, tid, st);
-  for (int64_t kb = klo / C; kb <= tile; ++kb) {
-    TT::write(sK, sV, tid, st);
-    if (kb < tile) TT::issue(rk, rv, kb + 1, tid, st);
+  if (NBUF == 2 && window <= C) {
+    // The band of a window of at most C keys is blocks tile-1 and tile
+    // (block -1 reads zeros and is masked): straight-line code, each block
+    // in its own LDS copy, two barriers.
+    TT::issue(rk, rv, tile - 1, tid, st);
+    TT::write(sK[0], sV[0], tid, st);
+    TT::issue(rk, rv, tile, tid, st);
     lds_barrier();
-    TT::block(sK, sV, kb, qi, window, c, bq, ones, O, m, lane);
-    lds_barrier();  // every wave is done with the block before it is replaced
+    TT::block(sK[0], sV[0], tile - 1, qi, window, c, bq, ones, O, m, lane);
+    TT::write(sK[NBUF - 1], sV[NBUF - 1], tid, st);
+    lds_barrier();
+    TT::block(sK[NBUF - 1], sV[NBUF - 1], tile, qi, window, c, bq, ones, O, m, lane);
+  } else {
+    const int64_t klo = i0 - window + 1 > 0 ? i0 - window + 1 : 0;
+    TT::issue(rk, rv, klo / C, tid, st);
+    for (int64_t kb = klo / C; kb <= tile; ++kb) {
+      TT::write(sK[0], sV[0], tid, st);
+      if (kb < tile) TT::issue(rk, rv, kb + 1, tid, st);
+      lds_barrier();
+      TT::block(sK[0], sV[0], kb, qi, window, c, bq, ones, O, m, lane);
+      lds_barrier();  // every wave is done with the block before it is replaced
+    }
   }
   TT::store(ry, qi, O, lane);
 }
