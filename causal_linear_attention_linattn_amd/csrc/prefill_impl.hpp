@@ -270,8 +270,11 @@ struct ChunkTiles {
 
   // key rows for the scores: lane (key jt, g) slot t <-> feature 32 kbs + 8 g + t
   __device__ static __forceinline__ frag k_rows(const T* sK, int jt, int kbs, int lane) {
-    const int f0 = 32 * kbs + 8 * (lane >> 4);
-    if (f0 >= DK) return E::zero();
+    if (32 * kbs >= DK) return E::zero();
+    // Lanes whose features lie past DK meet zero query slots (the operand
+    // builders zero every padded feature), so they read an in-range block
+    // rather than branch around the load: finite times zero adds nothing.
+    const int f0 = (32 * kbs + 8 * (lane >> 4)) & (DK - 1);
     if constexpr (BF)
       return E::load8(sK + RTK::off(jt, f0 >> 3));
     else
