@@ -22,7 +22,10 @@
 // across all columns.  The bf16 Taylor kernels have NW = 8 (kChunkWaves);
 // in their output kernels waves 4..7 own every state row tile and waves
 // 0..3 none (the role split below), and in their segment-sum kernels wave w
-// owns tiles w, w+8, ....  A bf16 (or fp32) copy of S' in LDS, laid out
+// owns tiles w, w+8, ....  The plain bf16 ELU1 segment-sum kernel at
+// d_k = 64 also has NW = 8: waves w and w+4 share row tile w & 3, wave w
+// owning column tiles 0..2 and wave w+4 the rest (the column split).  A
+// bf16 (or fp32) copy of S' in LDS, laid out
 // column-major, feeds the inter term of every output wave.  K, V tiles are
 // staged through LDS (bf16 row-major, read transposed; fp32 transposed) so
 // that every MFMA operand is one or two LDS reads; the next chunks' global
@@ -53,9 +56,16 @@ namespace linattn {
 // one MI355X at B=8 H=16 N=2048: 111.7 -> 106.6 us per call with every wave
 // doing both, 79.8 -> 70.7 us from the role split, and for the gated form
 // 107.2 -> 83.6 us (4 waves -> 8 split; 8 waves without the split spilled).
-// Float tiles keep 4 waves.
-template <int MAP, typename T, bool GATED>
-constexpr int kChunkWaves = MAP != MAP_ELU1 && sizeof(T) == 2 ? 8 : 4;
+// Float tiles keep 4 waves.  The plain bf16 ELU1 segment-sum kernel at
+// d_k = 64 also runs 8 waves: its 4 state row tiles are each shared by two
+// waves that own different column tiles (the column split below), so that
+// each SIMD holds two waves of a walk whose per-chunk chain is short.
+template <int MAP, typename T, int DK, bool GATED, bool OUT>
+constexpr int kChunkWaves =
+    (MAP != MAP_ELU1 && sizeof(T) == 2) ||
+            (MAP == MAP_ELU1 && sizeof(T) == 2 && DK == 64 && !GATED && !OUT)
+        ? 8
+        : 4;
 
 template <int MAP, typename T, int DK, int DV, int NWAVES = 4>
 struct PrefillShape : StateShape<MAP, DK, DV> {
@@ -362,8 +372,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int MAP, typename T, int DK, int DV, bool OUT, bool GATED>
-__global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kernel(PrefillArgs a) {
-  using SH = PrefillShape<MAP, T, DK, DV, kChunkWaves<MAP, T, GATED>>;
+__global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void chunk_kernel(PrefillArgs a) {
+  using SH = PrefillShape<MAP, T, DK, DV, kChunkWaves<MAP, T, DK, GATED, OUT>>;
   using E = Elem<T>;
   using frag = typename E::frag;
   constexpr bool BF = sizeof(T) == 2;
@@ -454,14 +464,20 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
   // straight-line code with registers of its own, and both pass the same
   // barriers.  Other kernels run one walk in which every wave does both.
   auto walk = [&](auto role_c) __attribute__((always_inline)) {
-    constexpr int ROLE = decltype(role_c)::value;  // 1: outputs, 2: state
+    // 1: outputs, 2: state (Taylor output kernels); 3, 4: the column halves
+    // of the ELU1 segment sums
+    constexpr int ROLE = decltype(role_c)::value;
     const bool qwave_r = ROLE == 1;
-    constexpr int kMT = ROLE == 1 ? 1 : (SH::NRT + 3) / 4;
-    static_assert(MAP != MAP_ELU1 && SH::NRT == 18, "the split owns 16 + 2 tiles");
+    constexpr int kMT = ROLE == 1 || ROLE >= 3 ? 1 : (SH::NRT + 3) / 4;
+    static_assert(ROLE >= 3 || (MAP != MAP_ELU1 && SH::NRT == 18), "the split owns 16 + 2 tiles");
+    static_assert(ROLE < 3 || (!OUT && SH::NRT == 4), "the column split pairs waves w, w + 4");
     // state row tile m of this wave (a tile index >= NRT means none)
     auto row_tile = [&](int m) __attribute__((always_inline)) -> int {
-      return ROLE == 1 ? SH::NRT + 64 : (w - 4) + 4 * m;
+      return ROLE == 1 ? SH::NRT + 64 : ROLE == 2 ? (w - 4) + 4 * m : (w & 3);
     };
+    // the state column tiles this wave owns
+    constexpr int kCT0 = ROLE == 4 ? (NCT + 1) / 2 : 0;
+    constexpr int kCT1 = ROLE == 3 ? (NCT + 1) / 2 : NCT;
     const int tid_o = tid, lane_o = lane, i16_o = i16, g_o = g;
     {
       // mutable copies of the lane indices (see opaque_if in the walk)
@@ -475,10 +491,16 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, GATED>)) void chunk_kerne
       walk(std::integral_constant<int, 1>{});
     else
       walk(std::integral_constant<int, 2>{});
+  } else if constexpr (MAP == MAP_ELU1 && NW == 8) {
+    if (w < 4)
+      walk(std::integral_constant<int, 3>{});
+    else
+      walk(std::integral_constant<int, 4>{});
   } else {
     constexpr int ROLE = 0;  // every wave: outputs (if any) and state
     const bool qwave_r = qwave;
     constexpr int kMT = SH::MAXRT;
+    constexpr int kCT0 = 0, kCT1 = NCT;
     auto row_tile = [&](int m) __attribute__((always_inline)) -> int { return w + NW * m; };
 #include "chunk_walk.inc"
   }
@@ -559,10 +581,11 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(PrefillArgs a) {
 template <int MAP, typename T, int DK, int DV, bool GATED>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   using SS = StateShape<MAP, DK, DV>;
-  constexpr int NT = 64 * kChunkWaves<MAP, T, GATED>;
+  constexpr int NT = 64 * kChunkWaves<MAP, T, DK, GATED, true>;
+  constexpr int NT_SUM = 64 * kChunkWaves<MAP, T, DK, GATED, false>;
   if (a.nseg > 1) {
     hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, false, GATED>),
-                       dim3(a.BH * (a.nseg - 1) * a.sum_split), dim3(NT), 0, st, a);
+                       dim3(a.BH * (a.nseg - 1) * a.sum_split), dim3(NT_SUM), 0, st, a);
     if (a.prefix_mode == 2) {
       hipLaunchKernelGGL((seg_scan_kernel<MAP, DK, DV>),
                          dim3((unsigned)(a.BH * (SS::SLOT / 4 / kScanCols))), dim3(256), 0,
