@@ -457,12 +457,15 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void ch
                             GATED ? (uint32_t)ntok * 4u : 0u);
 
   // ------------------------------------------------------------ roles ----
-  // The 8-wave output kernels run two specialised walks side by side: waves
-  // 0-3 make the chunk's outputs and own no state; waves 4-7 own every state
-  // row tile (tiles w-4, w, w+4, w+8 of the pair features, then the
-  // constant/linear tiles 16 and 17 on waves 4 and 5).  Each walk is
-  // straight-line code with registers of its own, and both pass the same
-  // barriers.  Other kernels run one walk in which every wave does both.
+  // The 8-wave Taylor output kernels run two specialised walks side by
+  // side: waves 0-3 make the chunk's outputs and own no state; waves 4-7 own
+  // every state row tile (tiles w-4, w, w+4, w+8 of the pair features, then
+  // the constant/linear tiles 16 and 17 on waves 4 and 5).  The 8-wave ELU1
+  // segment-sum kernel runs two column halves: waves w and w+4 share row
+  // tile w & 3, wave w owning its first column tiles and wave w+4 the rest.
+  // Each walk is straight-line code with registers of its own, and all pass
+  // the same barriers.  Other kernels run one walk in which every wave does
+  // both outputs and state.
   auto walk = [&](auto role_c) __attribute__((always_inline)) {
     // 1: outputs, 2: state (Taylor output kernels); 3, 4: the column halves
     // of the ELU1 segment sums
