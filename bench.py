@@ -28,6 +28,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import platform
 import sys
 import time
@@ -348,16 +349,30 @@ DIGEST_FILES = {
 }
 
 
+_CODE_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|\s+', re.S)
+
+
+def code_text(src):
+    """C++ source with comments removed and whitespace runs collapsed, so
+    that only edits which can change the compiled code change its hash."""
+    def sub(m):
+        t = m.group(0)
+        if t.startswith("//") or t.startswith("/*") or t.isspace():
+            return " "
+        return t
+    return re.sub(r" +", " ", _CODE_TOKENS.sub(sub, src)).strip()
+
+
 def csrc_digest(kind="prefill"):
-    """Hash of the HIP sources of one kernel family; a traffic figure is
-    valid only for this hash."""
+    """Hash of the code (comments and layout excluded) of the HIP sources of
+    one kernel family; a traffic figure is valid only for this hash."""
     import hashlib
 
     d = hashlib.sha256()
     csrc = os.path.join(ROOT, "causal_linear_attention_linattn_amd", "csrc")
     for name in DIGEST_FILES[kind]:
-        with open(os.path.join(csrc, name), "rb") as f:
-            d.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            d.update(name.encode() + b"\0" + code_text(f.read()).encode())
     return d.hexdigest()[:16]
 
 

@@ -256,3 +256,21 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_traffic_digest_follows_code_not_comments():
+    """The digest that keys recorded traffic changes with the code of a
+    kernel family and not with its comments or layout."""
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    a = 'int f(int x) { // doubles\n  return 2 * x; /* was 3 */ }\nconst char* s = "a // b";'
+    b = 'int f(int x) {\n\n    return 2 * x;\n}\n// note\nconst char* s = "a // b";'
+    c = 'int f(int x) { return 3 * x; }\nconst char* s = "a // b";'
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
+    assert '"a // b"' in bench.code_text(a)
+    for kind in bench.DIGEST_FILES:
+        assert len(bench.csrc_digest(kind)) == 16
