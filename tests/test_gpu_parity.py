@@ -172,6 +172,35 @@ def test_prefill_continues_from_state(fmap, d_k, d_v, dtype):
     assert state_err(ops.to_numpy64(S_io), S_ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64),
+                                         ("taylor2sym", 16, 32)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seg_len", [0, 64])
+def test_prefill_from_arbitrary_state(fmap, d_k, d_v, dtype, seg_len):
+    """An initial state that no prefill produced: S_in drawn at random (so
+    the two rows of a Taylor pair need not agree) and z_in a real running
+    sum (so every denominator stays positive).  Outputs and the returned
+    state follow the recurrence from exactly that state, through one
+    segment or several."""
+    _log(f"prefill from an arbitrary state {fmap} {dtype} seg_len={seg_len}")
+    scale = _qk_scale(fmap)
+    q0, k0, v0 = synth.draw_qkv(1, 3, 100, d_k, d_v, seed=11, dtype="f32", qk_scale=scale)
+    z_in = oracle.attention_recurrent(q0.f64(), k0.f64(), v0.f64(), fmap)[2]
+    D = oracle.feature_dim(fmap, d_k)
+    S_in = np.random.default_rng(12).standard_normal((1, 3, D, d_v)) * 4.0
+    S32, z32 = S_in.astype(np.float32), z_in.astype(np.float32)
+    q, k, v = synth.draw_qkv(1, 3, 300, d_k, d_v, seed=13, dtype=dtype, qk_scale=scale)
+    y_ref, S_ref, z_ref = oracle.attention_recurrent(q.f64(), k.f64(), v.f64(), fmap,
+                                                     S0=S32.astype(np.float64),
+                                                     z0=z32.astype(np.float64))
+    st = (torch.from_numpy(S32).to(DEV), torch.from_numpy(z32).to(DEV))
+    y, (S, z) = gpu_prefill(q, k, v, fmap, state=st, return_state=True, seg_len=seg_len)
+    tol = TOL[dtype]
+    assert row_err(ops.to_numpy64(y), y_ref) <= tol
+    assert state_err(ops.to_numpy64(S), S_ref) <= tol
+    assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
+
+
 @pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64)])
 def test_prefill_deterministic_and_segment_invariant(fmap, d_k, d_v):
     _log(f"determinism / segment invariance {fmap}")
