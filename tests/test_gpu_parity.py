@@ -202,6 +202,36 @@ def test_prefill_from_arbitrary_state(fmap, d_k, d_v, dtype, seg_len):
 
 
 @pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seg_len", [0, 64])
+def test_prefill_gated_from_arbitrary_state(fmap, d_k, d_v, dtype, seg_len):
+    """The gated prefill from a random initial state (as above), with decays
+    in [0.99, 1) so that the state still weighs at the end: the initial
+    state, its rows that do not agree included, decays with the sequence."""
+    _log(f"gated prefill from an arbitrary state {fmap} {dtype} seg_len={seg_len}")
+    scale = _qk_scale(fmap)
+    q0, k0, v0 = synth.draw_qkv(1, 3, 100, d_k, d_v, seed=21, dtype="f32", qk_scale=scale)
+    z_in = oracle.attention_recurrent(q0.f64(), k0.f64(), v0.f64(), fmap)[2]
+    D = oracle.feature_dim(fmap, d_k)
+    S_in = np.random.default_rng(22).standard_normal((1, 3, D, d_v)) * 4.0
+    S32, z32 = S_in.astype(np.float32), z_in.astype(np.float32)
+    q, k, v = synth.draw_qkv(1, 3, 300, d_k, d_v, seed=23, dtype=dtype, qk_scale=scale)
+    a = synth.draw_gate(1, 3, 300, seed=23, lo=0.99)
+    y_ref, S_ref, z_ref = oracle.attention_gated_recurrent(
+        q.f64(), k.f64(), v.f64(), a.astype(np.float64), fmap,
+        S0=S32.astype(np.float64), z0=z32.astype(np.float64))
+    st = (torch.from_numpy(S32).to(DEV), torch.from_numpy(z32).to(DEV))
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    y, (S, z) = ops.prefill_gated(qd, kd, vd, _gate_dev(a), fmap, state=st, return_state=True,
+                                  seg_len=seg_len)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert row_err(ops.to_numpy64(y), y_ref) <= tol
+    assert state_err(ops.to_numpy64(S), S_ref) <= tol
+    assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
+
+
+@pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64)])
 def test_prefill_deterministic_and_segment_invariant(fmap, d_k, d_v):
     _log(f"determinism / segment invariance {fmap}")
     scale = _qk_scale(fmap)
