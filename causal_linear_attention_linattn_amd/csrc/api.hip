@@ -275,8 +275,18 @@ linattn_status_t prefill_common(int map, int dtype, int64_t B, int64_t H,
   a.seg_chunks = seg_chunks;
   a.sum_split = sum_split(map, BH, nseg, seg_chunks);
   a.nslot = nseg * a.sum_split;
-  a.prefix_mode =
-      nseg == 1 ? 0 : ((nseg - 1) * a.sum_split <= kDirectPrefixMax - 1 ? 1 : 2);
+  // With several segments the output workgroups of one head run on
+  // different XCDs in no fixed order, and the last one writes S_out / z_out
+  // when it ends.  If those alias S_in / z_in, no output workgroup may read
+  // the initial state itself: the scan kernel (prefix_mode 2) folds it into
+  // the workspace prefixes in an earlier launch.  With one segment the
+  // workgroup that reads the state is the one that writes it, after its
+  // first chunk has consumed what it read.
+  const bool in_place = (S_out != nullptr && S_out == S_in) ||
+                        (z_out != nullptr && z_out == z_in);
+  a.prefix_mode = nseg == 1 ? 0
+                  : (!in_place && (nseg - 1) * a.sum_split <= kDirectPrefixMax - 1) ? 1
+                                                                                   : 2;
   a.sym = map == LINATTN_MAP_TAYLOR2_SYM ? 1 : 0;
   a.gate = gated ? gate : nullptr;
   a.ws_log = gated && nseg > 1

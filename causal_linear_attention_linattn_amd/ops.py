@@ -116,6 +116,8 @@ def _stream(t: torch.Tensor):
 
 
 def _need_cuda(*ts):
+    """Every given tensor lives on one GPU device and is contiguous."""
+    dev = None
     for t in ts:
         if t is None:
             continue
@@ -123,6 +125,37 @@ def _need_cuda(*ts):
             raise ValueError("linattn tensors must live on a GPU device")
         if not t.is_contiguous():
             raise ValueError("linattn tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"linattn tensors must share one device ({dev} vs {t.device})")
+
+
+def _expect(name, t, shape, dtype):
+    """t has exactly this shape and dtype (checked before any device use, so
+    a mis-sized buffer never reaches the library, which sizes every access
+    from the shape arguments)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _qkv(q, k, v, ndim):
+    """q, k [..., d_k] and v [..., d_v] over the same leading dims, one dtype."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dim() != ndim:
+            raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1]:
+        raise ValueError(f"expected q, k of one shape and v with the same leading dims; "
+                         f"got {tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    _dtype_id(q)
 
 
 def feature_dim(fmap: str, d_k: int) -> int:
@@ -145,6 +178,9 @@ def workspace_bytes(fmap, dtype, B, H, N, d_k, d_v, seg_len=0) -> int:
 def feature_map(x: torch.Tensor, fmap: str) -> torch.Tensor:
     """phi(x) over the last axis, float32 [..., D] (test/inspection export)."""
     L = load_library()
+    if not isinstance(x, torch.Tensor) or x.dim() < 1:
+        raise TypeError("x must be a torch.Tensor with a feature axis")
+    _dtype_id(x)
     _need_cuda(x)
     d_k = x.shape[-1]
     D = feature_dim(fmap, d_k)
@@ -176,24 +212,21 @@ def prefill_gated(q, k, v, gate, fmap: str, *, normalize=True, state=None,
 
 def _prefill(q, k, v, gate, normalize, fmap, state, return_state, seg_len, out):
     L = load_library()
-    _need_cuda(q, k, v)
-    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
-        raise ValueError("expected q, k [B,H,N,d_k] and v [B,H,N,d_v]")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k, v must share one dtype")
+    _qkv(q, k, v, 4)
     B, H, N, d_k = q.shape
     d_v = v.shape[-1]
     D = feature_dim(fmap, d_k)
-    y = out if out is not None else torch.empty_like(v)
-    _need_cuda(y)
+    if out is not None:
+        _expect("out", out, v.shape, v.dtype)
     S_in = z_in = None
     if state is not None:
         S_in, z_in = state
-        _need_cuda(S_in, z_in)
-        if S_in.dtype != torch.float32 or z_in.dtype != torch.float32:
-            raise TypeError("state tensors must be float32")
-        if tuple(S_in.shape) != (B, H, D, d_v) or tuple(z_in.shape) != (B, H, D):
-            raise ValueError("state shapes must be [B,H,D,d_v] and [B,H,D]")
+        _expect("state S", S_in, (B, H, D, d_v), torch.float32)
+        _expect("state z", z_in, (B, H, D), torch.float32)
+    if gate is not None:
+        _expect("gate", gate, (B, H, N), torch.float32)
+    _need_cuda(q, k, v, out, S_in, z_in, gate)
+    y = out if out is not None else torch.empty_like(v)
     S_out = z_out = None
     if return_state:
         S_out = torch.empty((B, H, D, d_v), dtype=torch.float32, device=q.device)
@@ -206,9 +239,6 @@ def _prefill(q, k, v, gate, normalize, fmap, state, return_state, seg_len, out):
                                  _ptr(z_in), _ptr(S_out), _ptr(z_out), seg_len,
                                  _ptr(ws), nws, _stream(q)))
     else:
-        _need_cuda(gate)
-        if gate.dtype != torch.float32 or tuple(gate.shape) != (B, H, N):
-            raise ValueError("gate must be float32 [B, H, N]")
         _check(L.linattn_prefill_gated(_map_id(fmap), _dtype_id(q), B, H, N, d_k, d_v,
                                        _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                                        1 if normalize else 0, _ptr(y), _ptr(S_in),
@@ -232,25 +262,23 @@ def decode_step_gated(q, k, v, gate, S, z, fmap: str, *, normalize=True, out=Non
 
 def _decode(q, k, v, gate, normalize, S, z, fmap, out):
     L = load_library()
-    _need_cuda(q, k, v, S, z)
-    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
-        raise ValueError("expected q, k [B,H,d_k] and v [B,H,d_v]")
+    _qkv(q, k, v, 3)
     B, H, d_k = q.shape
     d_v = v.shape[-1]
     D = feature_dim(fmap, d_k)
-    if S.dtype != torch.float32 or z.dtype != torch.float32:
-        raise TypeError("state tensors must be float32")
-    if tuple(S.shape) != (B, H, D, d_v) or tuple(z.shape) != (B, H, D):
-        raise ValueError("state shapes must be [B,H,D,d_v] and [B,H,D]")
+    _expect("S", S, (B, H, D, d_v), torch.float32)
+    _expect("z", z, (B, H, D), torch.float32)
+    if out is not None:
+        _expect("out", out, v.shape, v.dtype)
+    if gate is not None:
+        _expect("gate", gate, (B, H), torch.float32)
+    _need_cuda(q, k, v, S, z, out, gate)
     y = out if out is not None else torch.empty_like(v)
     if gate is None:
         _check(L.linattn_decode_step(_map_id(fmap), _dtype_id(q), B, H, d_k, d_v,
                                      _ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z),
                                      _ptr(y), _stream(q)))
     else:
-        _need_cuda(gate)
-        if gate.dtype != torch.float32 or tuple(gate.shape) != (B, H):
-            raise ValueError("gate must be float32 [B, H]")
         _check(L.linattn_decode_step_gated(_map_id(fmap), _dtype_id(q), B, H, d_k, d_v,
                                            _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                                            1 if normalize else 0, _ptr(S), _ptr(z),
@@ -264,15 +292,15 @@ def swa_prefill(q, k, v, window: int, *, scale=None, return_cache=False, out=Non
     scale defaults to 1/sqrt(d).  return_cache: also return the ring caches
     (k_cache, v_cache) [B, H, window, d] for swa_decode_step."""
     L = load_library()
-    _need_cuda(q, k, v)
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+    _qkv(q, k, v, 4)
+    if v.shape != q.shape:
         raise ValueError("expected q, k, v [B,H,N,d] of one shape")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k, v must share one dtype")
     B, H, N, d = q.shape
     sc = float(d) ** -0.5 if scale is None else float(scale)
+    if out is not None:
+        _expect("out", out, v.shape, v.dtype)
+    _need_cuda(q, k, v, out)
     y = out if out is not None else torch.empty_like(v)
-    _need_cuda(y)
     kc = vc = None
     if return_cache:
         kc = torch.empty((B, H, window, d), dtype=q.dtype, device=q.device)
@@ -288,12 +316,16 @@ def swa_decode_step(q, k, v, pos, k_cache, v_cache, window: int, *, scale=None, 
     """One sliding-window generation step; q, k, v [B,H,d]; pos int64 [B]
     (0-based position of this token per sequence); caches updated in place."""
     L = load_library()
-    _need_cuda(q, k, v, pos, k_cache, v_cache)
+    _qkv(q, k, v, 3)
+    if v.shape != q.shape:
+        raise ValueError("expected q, k, v [B,H,d] of one shape")
     B, H, d = q.shape
-    if pos.dtype != torch.int64 or tuple(pos.shape) != (B,):
-        raise ValueError("pos must be int64 [B]")
-    if tuple(k_cache.shape) != (B, H, window, d) or v_cache.shape != k_cache.shape:
-        raise ValueError("caches must be [B, H, window, d]")
+    _expect("pos", pos, (B,), torch.int64)
+    _expect("k_cache", k_cache, (B, H, window, d), q.dtype)
+    _expect("v_cache", v_cache, (B, H, window, d), q.dtype)
+    if out is not None:
+        _expect("out", out, v.shape, v.dtype)
+    _need_cuda(q, k, v, pos, k_cache, v_cache, out)
     sc = float(d) ** -0.5 if scale is None else float(scale)
     y = out if out is not None else torch.empty_like(v)
     _check(L.linattn_swa_decode_step(_dtype_id(q), B, H, d, window, sc, _ptr(q), _ptr(k),

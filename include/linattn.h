@@ -129,7 +129,10 @@ size_t linattn_prefill_workspace_bytes(int map, int dtype, int64_t B,
  *   S_out, z_out [B, H, D, d_v], [B, H, D] float32: the state after token N,
  *               or both NULL.  S_out may be the same pointer as S_in and
  *               z_out the same as z_in (in-place continuation); any other
- *               overlap is an error.
+ *               overlap is an error.  In place, a plan of several segments
+ *               per head always forms the segment prefixes in a separate
+ *               launch that reads S_in, z_in before any output workgroup
+ *               runs, so no workgroup can read a state already overwritten.
  *   seg_len     tokens per workgroup segment along N: 0 = library choice,
  *               else a positive multiple of 64.  Results agree for every
  *               choice to rounding; each choice is deterministic.

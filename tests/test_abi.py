@@ -274,3 +274,63 @@ def test_traffic_digest_follows_code_not_comments():
     assert '"a // b"' in bench.code_text(a)
     for kind in bench.DIGEST_FILES:
         assert len(bench.csrc_digest(kind)) == 16
+
+
+def test_binding_rejects_mis_sized_buffers_before_the_library(lib):
+    """The Python binding checks the shape, dtype and device of every tensor,
+    out= included, before it calls the library (which sizes every device
+    access from the shape arguments).  Host tensors of valid shapes are
+    refused as host tensors; mis-shaped ones are refused for their shape or
+    dtype first, so these checks run here without a GPU."""
+    import torch
+
+    q = torch.zeros(1, 2, 8, 16)
+    k, v = q.clone(), q.clone()
+    with pytest.raises(ValueError, match="out must have shape"):
+        ops.prefill(q, k, v, "elu1", out=torch.zeros(1, 2, 8, 8))
+    with pytest.raises(TypeError, match="out must be"):
+        ops.prefill(q, k, v, "elu1", out=torch.zeros(1, 2, 8, 16, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="expected q, k"):
+        ops.prefill(q, torch.zeros(1, 2, 8, 32), v, "elu1")
+    with pytest.raises(TypeError, match="share one dtype"):
+        ops.prefill(q, k.bfloat16(), v, "elu1")
+    with pytest.raises(TypeError, match="not supported"):
+        ops.prefill(q.double(), k.double(), v.double(), "elu1")
+    with pytest.raises(ValueError, match="state S must have shape"):
+        ops.prefill(q, k, v, "elu1", state=(torch.zeros(1, 2, 16, 8), torch.zeros(1, 2, 16)))
+    with pytest.raises(ValueError, match="gate must have shape"):
+        ops.prefill_gated(q, k, v, torch.zeros(1, 2, 7), "elu1")
+    with pytest.raises(ValueError, match="GPU device"):
+        ops.prefill(q, k, v, "elu1")
+
+    q3 = torch.zeros(1, 2, 16)
+    S, z = torch.zeros(1, 2, 16, 16), torch.zeros(1, 2, 16)
+    with pytest.raises(ValueError, match="out must have shape"):
+        ops.decode_step(q3, q3, q3, S, z, "elu1", out=torch.zeros(1, 2, 8))
+    with pytest.raises(TypeError, match="out must be"):
+        ops.decode_step(q3, q3, q3, S, z, "elu1", out=torch.zeros(1, 2, 16).bfloat16())
+    with pytest.raises(ValueError, match="S must have shape"):
+        ops.decode_step(q3, q3, q3, torch.zeros(1, 2, 16, 8), z, "elu1")
+    with pytest.raises(TypeError, match="z must be"):
+        ops.decode_step(q3, q3, q3, S, z.double(), "elu1")
+    with pytest.raises(ValueError, match="gate must have shape"):
+        ops.decode_step_gated(q3, q3, q3, torch.zeros(2), S, z, "elu1")
+
+    kc = torch.zeros(1, 2, 4, 16)
+    pos = torch.zeros(1, dtype=torch.int64)
+    with pytest.raises(ValueError, match="k_cache must have shape"):
+        ops.swa_decode_step(q3, q3, q3, pos, torch.zeros(1, 2, 5, 16), kc, 4)
+    with pytest.raises(TypeError, match="v_cache must be"):
+        ops.swa_decode_step(q3, q3, q3, pos, kc, kc.bfloat16(), 4)
+    with pytest.raises(ValueError, match="expected q, k"):
+        ops.swa_decode_step(q3, torch.zeros(1, 2, 32), q3, pos, kc, kc.clone(), 4)
+    with pytest.raises(ValueError, match="one shape"):
+        ops.swa_decode_step(q3, q3, torch.zeros(1, 2, 32), pos, kc, kc.clone(), 4)
+    with pytest.raises(TypeError, match="pos must be"):
+        ops.swa_decode_step(q3, q3, q3, pos.int(), kc, kc.clone(), 4)
+    with pytest.raises(ValueError, match="out must have shape"):
+        ops.swa_decode_step(q3, q3, q3, pos, kc, kc.clone(), 4, out=torch.zeros(1, 2, 8))
+    with pytest.raises(ValueError, match="out must have shape"):
+        ops.swa_prefill(q, k, v, 4, out=torch.zeros(1, 2, 8, 8))
+    with pytest.raises(ValueError, match="GPU device"):
+        ops.swa_decode_step(q3, q3, q3, pos, kc, kc.clone(), 4)

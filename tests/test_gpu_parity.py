@@ -404,6 +404,89 @@ def test_prefill_graph_replays_match_eager(case):
             assert torch.equal(a, b), (r, i)
 
 
+# ------------------------------------------- in place, many segments ------
+def _segment_ends(t0, n, seg_len):
+    """First and last row (global index) of every segment of one call."""
+    rows = set()
+    for s in range(0, n, seg_len):
+        rows.add(t0 + s)
+        rows.add(t0 + min(s + seg_len, n) - 1)
+    return rows
+
+
+@pytest.mark.parametrize("fmap,d_k,d_v,B,H", [("elu1", 64, 64, 32, 8),
+                                              ("taylor2", 16, 64, 8, 8),
+                                              ("taylor2sym", 16, 32, 8, 8)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_prefill_in_place_many_segments(fmap, d_k, d_v, B, H, gated):
+    """Continuation in place (S_out is S_in, z_out is z_in) through calls
+    of 1, 4, 3 and 9 segments per head (seg_len 64, 128, 64) with many heads,
+    so that the segments of one head run on different XCDs in no fixed
+    order.  The first and last row of every segment of every call and the
+    final state of every head follow the oracle's recurrence over the whole
+    concatenated sequence."""
+    if gated:
+        B //= 2   # the gated row oracle forms running decay products per row
+    _log(f"prefill in place, many segments {fmap} gated={gated} B={B} H={H}")
+    parts = [(100, 0), (256, 64), (384, 128), (576, 64)]   # (tokens, seg_len)
+    N = sum(n for n, _ in parts)
+    q, k, v = synth.draw_qkv(B, H, N, d_k, d_v, seed=21, dtype="bf16",
+                             qk_scale=_qk_scale(fmap))
+    a = synth.draw_gate(B, H, N, seed=21, lo=0.9, reset_p=0.002) if gated else None
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    ad = _gate_dev(a) if gated else None
+    D = oracle.feature_dim(fmap, d_k)
+    S = torch.zeros((B, H, D, d_v), dtype=torch.float32, device=DEV)
+    z = torch.zeros((B, H, D), dtype=torch.float32, device=DEV)
+    L = ops.load_library()
+    m = ops.MAPS[fmap]
+    y = torch.empty_like(vd)
+    rows = set()
+    t0 = 0
+    for n, seg_len in parts:
+        sl = lambda x: x[:, :, t0:t0 + n].contiguous()
+        qs, ks, vs = sl(qd), sl(kd), sl(vd)
+        ys = torch.empty_like(vs)
+        nws = ops.workspace_bytes(fmap, torch.bfloat16, B, H, n, d_k, d_v, seg_len)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+        if gated:
+            gs = ad[:, :, t0:t0 + n].contiguous()
+            rc = L.linattn_prefill_gated(m, 1, B, H, n, d_k, d_v, ops._ptr(qs), ops._ptr(ks),
+                                         ops._ptr(vs), ops._ptr(gs), 1, ops._ptr(ys),
+                                         ops._ptr(S), ops._ptr(z), ops._ptr(S), ops._ptr(z),
+                                         seg_len, ops._ptr(ws), nws, ops._stream(qd))
+        else:
+            rc = L.linattn_prefill(m, 1, B, H, n, d_k, d_v, ops._ptr(qs), ops._ptr(ks),
+                                   ops._ptr(vs), ops._ptr(ys), ops._ptr(S), ops._ptr(z),
+                                   ops._ptr(S), ops._ptr(z), seg_len, ops._ptr(ws), nws,
+                                   ops._stream(qd))
+        assert rc == 0
+        y[:, :, t0:t0 + n] = ys
+        rows |= _segment_ends(t0, n, seg_len or n)
+        t0 += n
+    torch.cuda.synchronize()
+    y = ops.to_numpy64(y)
+    S = ops.to_numpy64(S)
+    z = ops.to_numpy64(z)
+    q64, k64, v64 = q.f64(), k.f64(), v.f64()
+    rng = np.random.default_rng(22)
+    rows = sorted(rows | set(rng.integers(0, N, 8).tolist()))
+    for b in range(B):
+        for h in range(H):
+            if gated:
+                ref = oracle.attention_gated_rows(q64[b, h], k64[b, h], v64[b, h],
+                                                  a[b, h].astype(np.float64), fmap, rows)
+            else:
+                ref = oracle.attention_rows(q64[b, h], k64[b, h], v64[b, h], fmap, rows)
+            assert row_err(y[b, h, rows], ref) <= TOL["bf16"], (b, h)
+    if gated:
+        S_ref, z_ref = oracle.gated_final_state(k64, v64, a.astype(np.float64), fmap)
+    else:
+        S_ref, z_ref = oracle.final_state(k64, v64, fmap)
+    assert state_err(S, S_ref) <= TOL["bf16"]
+    assert state_err(z[..., None], z_ref[..., None]) <= TOL["bf16"]
+
+
 # ------------------------------------------------------- gated form ------
 def _gate_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
