@@ -7,6 +7,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "linattn.h"
 #include "shapes.hpp"
 
@@ -193,6 +195,38 @@ hipError_t dispatch_decode(int map, int dtype, int64_t dk, int64_t dv,
   return hipErrorInvalidValue;
 }
 
+// The fixed device array behind linattn_prefill_noalloc: the prefill's
+// segment part sums live here instead of in a caller-provided workspace.
+// Each device the library runs on holds its own copy, zero at module load
+// and kept until the process ends.  Host code never names the array itself
+// (on the host its name is a stand-in, not a device address); it uses the
+// device address that hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+constexpr size_t kScratchBytes = LINATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device.
+hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 linattn_status_t prefill_common(int map, int dtype, int64_t B, int64_t H,
                                 int64_t N, int64_t d_k, int64_t d_v,
                                 const void* q, const void* k, const void* v,
@@ -200,7 +234,7 @@ linattn_status_t prefill_common(int map, int dtype, int64_t B, int64_t H,
                                 void* y, const float* S_in, const float* z_in,
                                 float* S_out, float* z_out, int64_t seg_len,
                                 void* workspace, size_t workspace_bytes_given,
-                                void* stream) {
+                                void* stream, bool fixed_scratch = false) {
   if (!valid_map(map) || !valid_dtype(dtype) || B <= 0 || H <= 0 || N <= 0 ||
       d_k <= 0 || d_v <= 0)
     return LINATTN_ERR_INVALID_ARGUMENT;
@@ -250,7 +284,15 @@ linattn_status_t prefill_common(int map, int dtype, int64_t B, int64_t H,
     if (overlap(outs[i], rg)) return LINATTN_ERR_INVALID_ARGUMENT;
 
   const size_t need = workspace_bytes(map, BH, d_k, d_v, nseg, seg_chunks);
-  if (need > 0) {
+  if (fixed_scratch) {
+    if (need > kScratchBytes) return LINATTN_ERR_SCRATCH;
+    workspace = nullptr;
+    if (need > 0) {
+      // the only HIP calls before the launch: the device and, on its first
+      // use there, the array's address (no allocation)
+      if (scratch_on_current_device(&workspace) != hipSuccess) return LINATTN_ERR_HIP;
+    }
+  } else if (need > 0) {
     if (workspace == nullptr || !aligned16(workspace) || workspace_bytes_given < need)
       return LINATTN_ERR_WORKSPACE;
     const Range rw{reinterpret_cast<const char*>(workspace), need};
@@ -386,6 +428,8 @@ const char* linattn_status_string(int status) {
       return "workspace missing or smaller than linattn_prefill_workspace_bytes()";
     case LINATTN_ERR_HIP:
       return "the HIP runtime reported an error while launching";
+    case LINATTN_ERR_SCRATCH:
+      return "linattn_prefill_noalloc: the call needs more scratch than the fixed device array holds (LINATTN_NOALLOC_SCRATCH_BYTES); use linattn_prefill with a workspace";
     default:
       return "unknown status";
   }
@@ -468,6 +512,17 @@ linattn_status_t linattn_prefill_gated(int map, int dtype, int64_t B, int64_t H,
   return prefill_common(map, dtype, B, H, N, d_k, d_v, q, k, v, true, gate, normalize,
                         y, S_in, z_in, S_out, z_out, seg_len, workspace,
                         workspace_bytes_given, stream);
+}
+
+linattn_status_t linattn_prefill_noalloc(int map, int dtype, int64_t B, int64_t H,
+                                         int64_t N, int64_t d_k, int64_t d_v,
+                                         const void* q, const void* k, const void* v,
+                                         void* y, const float* S_in, const float* z_in,
+                                         float* S_out, float* z_out, int64_t seg_len,
+                                         void* stream) {
+  return prefill_common(map, dtype, B, H, N, d_k, d_v, q, k, v, false, nullptr, 1,
+                        y, S_in, z_in, S_out, z_out, seg_len, nullptr, 0, stream,
+                        /*fixed_scratch=*/true);
 }
 
 linattn_status_t linattn_decode_step(int map, int dtype, int64_t B, int64_t H,

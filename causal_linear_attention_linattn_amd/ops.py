@@ -9,6 +9,8 @@ Entry points (same names as the C ABI in include/linattn.h):
     feature_map(x, fmap)                      -> phi(x) float32 [..., D]
     prefill(q, k, v, fmap, state=None, ...)   -> y (and the final state)
     decode_step(q, k, v, S, z, fmap)          -> y; S, z updated in place
+    prefill_noalloc(q, k, v, fmap, ...)       -> as prefill; the library's
+                                                 fixed scratch, no workspace
     prefill_gated(q, k, v, gate, fmap, ...)   -> y (and the final state)
     decode_step_gated(q, k, v, gate, S, z, fmap) -> y; S, z updated in place
     swa_prefill(q, k, v, window, ...)          -> y (and the ring cache)
@@ -28,7 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
 MAPS = {"elu1": 0, "taylor2": 1, "taylor2sym": 2}
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace",
-           4: "hip error"}
+           4: "hip error", 5: "fixed scratch too small"}
 
 _lib = None
 
@@ -73,6 +75,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.linattn_prefill_gated.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp,
                                         fp, i32, vp, fp, fp, fp, fp, i64, vp, sz, vp]
     L.linattn_prefill_gated.restype = i32
+    L.linattn_prefill_noalloc.argtypes = [i32, i32, i64, i64, i64, i64, i64, vp, vp, vp,
+                                          vp, fp, fp, fp, fp, i64, vp]
+    L.linattn_prefill_noalloc.restype = i32
     L.linattn_decode_step_gated.argtypes = [i32, i32, i64, i64, i64, i64, vp, vp, vp,
                                             fp, i32, fp, fp, vp, vp]
     L.linattn_decode_step_gated.restype = i32
@@ -202,6 +207,16 @@ def prefill(q, k, v, fmap: str, *, state=None, return_state=False,
     return _prefill(q, k, v, None, True, fmap, state, return_state, seg_len, out)
 
 
+def prefill_noalloc(q, k, v, fmap: str, *, state=None, return_state=False,
+                    seg_len: int = 0, out=None):
+    """prefill() through linattn_prefill_noalloc: the segment part sums go to
+    the library's fixed device array instead of a workspace (the library call
+    allocates nothing; this wrapper allocates y and the state only when they
+    are not passed in as out= / returned)."""
+    return _prefill(q, k, v, None, True, fmap, state, return_state, seg_len, out,
+                    noalloc=True)
+
+
 def prefill_gated(q, k, v, gate, fmap: str, *, normalize=True, state=None,
                   return_state=False, seg_len: int = 0, out=None):
     """Gated (scalar-decay) prefill: gate is float32 [B, H, N] holding a_t;
@@ -210,7 +225,8 @@ def prefill_gated(q, k, v, gate, fmap: str, *, normalize=True, state=None,
     return _prefill(q, k, v, gate, normalize, fmap, state, return_state, seg_len, out)
 
 
-def _prefill(q, k, v, gate, normalize, fmap, state, return_state, seg_len, out):
+def _prefill(q, k, v, gate, normalize, fmap, state, return_state, seg_len, out,
+             noalloc=False):
     L = load_library()
     _qkv(q, k, v, 4)
     B, H, N, d_k = q.shape
@@ -231,6 +247,12 @@ def _prefill(q, k, v, gate, normalize, fmap, state, return_state, seg_len, out):
     if return_state:
         S_out = torch.empty((B, H, D, d_v), dtype=torch.float32, device=q.device)
         z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    if noalloc:
+        _check(L.linattn_prefill_noalloc(_map_id(fmap), _dtype_id(q), B, H, N, d_k, d_v,
+                                         _ptr(q), _ptr(k), _ptr(v), _ptr(y), _ptr(S_in),
+                                         _ptr(z_in), _ptr(S_out), _ptr(z_out), seg_len,
+                                         _stream(q)))
+        return (y, (S_out, z_out)) if return_state else y
     nws = workspace_bytes(fmap, q.dtype, B, H, N, d_k, d_v, seg_len)
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=q.device)
     if gate is None:

@@ -32,7 +32,8 @@
  *
  * Conventions shared by every call:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
- *     library allocates and frees nothing and keeps no global state.
+ *     library allocates and frees nothing and keeps no global state, except
+ *     the fixed device array of linattn_prefill_noalloc.
  *   - Tensors are contiguous, row-major, and their base address is 16-byte
  *     aligned.  q, k, v, y share one element type (linattn_dtype_t); the
  *     states S, z are always float32.
@@ -66,8 +67,13 @@ typedef enum linattn_status {
   LINATTN_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, size <= 0, misaligned */
   LINATTN_ERR_UNSUPPORTED = 2,      /* valid but not built: map/dtype/d_k/d_v */
   LINATTN_ERR_WORKSPACE = 3,        /* workspace missing or too small */
-  LINATTN_ERR_HIP = 4               /* the HIP runtime rejected a launch */
+  LINATTN_ERR_HIP = 4,              /* the HIP runtime rejected a launch */
+  LINATTN_ERR_SCRATCH = 5           /* linattn_prefill_noalloc: the call needs
+                                       more than its fixed scratch array */
 } linattn_status_t;
+
+/* Bytes of the fixed device array of linattn_prefill_noalloc (per device). */
+#define LINATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum linattn_map {
   LINATTN_MAP_ELU1 = 0,
@@ -151,6 +157,33 @@ linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,
                                  const float* z_in, float* S_out, float* z_out,
                                  int64_t seg_len, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * linattn_prefill without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid allocation.  Every argument means what it means for
+ * linattn_prefill; the segment part sums go to a fixed device array that
+ * the library holds on each device it runs on (LINATTN_NOALLOC_SCRATCH_BYTES,
+ * 64 MiB, kept until the process ends).  The call allocates nothing and
+ * frees nothing; on its first use on a device it looks up that array's
+ * device address (the device current at the call, which must be the
+ * stream's device).
+ *   Returns LINATTN_ERR_SCRATCH, before anything is launched, when
+ *   linattn_prefill_workspace_bytes(map, dtype, B, H, N, d_k, d_v, seg_len)
+ *   exceeds LINATTN_NOALLOC_SCRATCH_BYTES (a Taylor part sum at d_v = 64
+ *   takes 92,160 bytes per head and part, so B=8 H=16 N=2048 needs 47 MB;
+ *   ELU1 at d = 64 takes 20,480); other errors as linattn_prefill.
+ *   All calls on one device share its array: two calls that may run at the
+ *   same time on one device (different streams, no ordering between them)
+ *   race and give wrong results.  Calls ordered on one stream are safe;
+ *   what a call leaves in the array does not matter to the next one.
+ */
+linattn_status_t linattn_prefill_noalloc(int map, int dtype, int64_t B, int64_t H,
+                                         int64_t N, int64_t d_k, int64_t d_v,
+                                         const void* q, const void* k, const void* v,
+                                         void* y, const float* S_in, const float* z_in,
+                                         float* S_out, float* z_out, int64_t seg_len,
+                                         void* stream);
 
 /*
  * Gated (scalar-decay) causal prefill.  The state is scaled by a per-token

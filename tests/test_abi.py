@@ -334,3 +334,19 @@ def test_binding_rejects_mis_sized_buffers_before_the_library(lib):
         ops.swa_prefill(q, k, v, 4, out=torch.zeros(1, 2, 8, 8))
     with pytest.raises(ValueError, match="GPU device"):
         ops.swa_decode_step(q3, q3, q3, pos, kc, kc.clone(), 4)
+
+
+def test_noalloc_rejects_calls_beyond_its_fixed_scratch(lib):
+    """linattn_prefill_noalloc refuses, before any HIP call, a plan whose part
+    sums exceed its fixed array: Taylor d_v = 64 at 128 heads in 128 segments
+    of one chunk needs 128 * 128 * 92160 bytes."""
+    need = lib.linattn_prefill_workspace_bytes(1, 1, 8, 16, 8192, 16, 64, 64)
+    assert need > 64 << 20
+    rc = lib.linattn_prefill_noalloc(
+        1, 1, 8, 16, 8192, 16, 64, A["q"], A["k"], A["v"], A["y"], None, None, None, None,
+        64, None)
+    assert rc == 5
+    assert b"fixed" in lib.linattn_status_string(5)
+    # argument errors still come first
+    assert lib.linattn_prefill_noalloc(1, 1, 8, 16, 8192, 16, 64, None, A["k"], A["v"],
+                                       A["y"], None, None, None, None, 64, None) == 1
