@@ -11,7 +11,9 @@ per step, all heads).  The same JSON line carries:
                 (D = 273), state seeded by the library's own prefill over a
                 1024-token prefix, 128 steps; steps/s and its HBM roofline
                 (algorithmic bytes: state read + written, q, k, v, y);
-  cpu_baseline  the float64 oracle on the host, on a bounded sample;
+  cpu_baseline  the float64 oracle on this host, on a bounded sample: the
+                (b, h) pairs split over one worker process per core (at
+                most 16, one BLAS thread each), and on one core alone;
   other_configs the Taylor-2 and 64K-token prefills, an N sweep (4K to
                 64K tokens) showing time linear in N, the gated
                 (scalar-decay) prefill on the headline and Taylor shapes, and
@@ -404,69 +406,175 @@ def copy_calibration(torch):
     print(json.dumps({"copy_calibration_bytes_each_way": n, "launches": 3}))
 
 
-def cpu_baseline(synth, budget_s=10.0):
-    """The float64 oracle (recurrent form) on whole batch elements of the
-    prefill workload, one element at a time, passing over the batch again
-    until the time budget is used."""
-    import numpy as np
+def host_identity():
+    """CPU model string and the cores this process may run on."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+# Worker processes of the CPU baselines: at most this many, one BLAS thread
+# each (a one-GPU box grants its job a share of 16 host cores).
+CPU_WORKERS_MAX = 16
+
+
+def _oracle_worker(kind, w, nworkers, budget_s, barrier, results):
+    """One worker of the multi-core oracle baseline (a spawned process).
+    Prefill: the float64 recurrence over the (b, h) pairs p = w, w + W, ...
+    of the headline workload, at most one batch element's worth of heads
+    per oracle call, repeated until the budget is spent.  Decode: the
+    128-step generation of the sequences b = w, w + W, ... (all heads) from
+    an unseeded state.  Inputs are drawn before the barrier; only the
+    oracle's own work is timed."""
     from threadpoolctl import threadpool_limits
+    import numpy as np
 
     import oracle
+    from causal_linear_attention_linattn_amd import synth
 
-    cfg = synth.WORKLOADS[PREFILL]
-    q, k, v = synth.workload_inputs(PREFILL, seed=0)
-    done_tokens = 0
-    spent = 0.0
     with threadpool_limits(limits=1):
-        while spent < budget_s:
-            for b in range(cfg["B"]):
-                q64, k64, v64 = (synth.bf16_bits_to_f32(x.data[b:b + 1]).astype(np.float64)
-                                 for x in (q, k, v))
-                t0 = time.perf_counter()
-                y, _, _ = oracle.attention_recurrent(q64, k64, v64, cfg["fmap"])
-                spent += time.perf_counter() - t0
-                assert np.all(np.isfinite(y))
-                done_tokens += cfg["N"]
-                if spent >= budget_s:
-                    break
-    return {"value": done_tokens / spent, "unit": "tokens/s", "cores": 1,
+        if kind == "prefill":
+            cfg = synth.WORKLOADS[PREFILL]
+            q, k, v = (x.f64().reshape(cfg["B"] * cfg["H"], cfg["N"], -1)
+                       for x in synth.workload_inputs(PREFILL, seed=0))
+            pairs = list(range(w, cfg["B"] * cfg["H"], nworkers))
+            q, k, v = q[pairs], k[pairs], v[pairs]
+            unit = len(pairs) * cfg["N"]            # token-heads per pass
+        else:
+            cfg = synth.WORKLOADS[DECODE]
+            seqs = list(range(w, cfg["B"], nworkers))
+            # the step tokens of the generation workload (its stream 1); the
+            # state starts unseeded, S = 0 and z = 1 (the oracle's step costs
+            # the same for any state values)
+            sq, sk, sv = synth.draw_qkv(cfg["B"], cfg["H"], cfg["steps"], cfg["d_k"],
+                                        cfg["d_v"], 0, stream=1, dtype=cfg["dtype"],
+                                        qk_scale=cfg["qk_scale"])
+            q, k, v = (x.f64()[seqs] for x in (sq, sk, sv))
+            D = feature_dim("taylor2", cfg["d_k"])
+            S0 = np.zeros((len(seqs), cfg["H"], D, cfg["d_v"]))
+            z0 = np.ones((len(seqs), cfg["H"], D))
+            unit = len(seqs)                        # sequence-steps per step
+        barrier.wait()
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            if kind == "prefill":
+                for g0 in range(0, len(pairs), cfg["H"]):
+                    sl = slice(g0, g0 + cfg["H"])
+                    y, _, _ = oracle.attention_recurrent(q[sl], k[sl], v[sl], cfg["fmap"])
+                done += unit
+            else:
+                S, z = S0, z0
+                for t in range(cfg["steps"]):
+                    y, S, z = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], S, z,
+                                                 "taylor2")
+                done += unit * cfg["steps"]
+            assert np.all(np.isfinite(y))
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        t1 = time.perf_counter()
+    results.put((w, done, t0, t1))
+
+
+def _oracle_parallel(kind, nworkers, budget_s):
+    """Run the oracle in nworkers spawned processes at once; returns
+    (units done, wall seconds from the first start to the last end)."""
+    import multiprocessing as mp
+
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(nworkers)
+    results = ctx.Queue()
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                            "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        procs = [ctx.Process(target=_oracle_worker,
+                             args=(kind, w, nworkers, budget_s, barrier, results))
+                 for w in range(nworkers)]
+        for p_ in procs:
+            p_.start()
+        out = [results.get(timeout=budget_s * 4 + 300) for _ in procs]
+        for p_ in procs:
+            p_.join()
+    finally:
+        for k, val in saved.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
+    done = sum(o[1] for o in out)
+    wall = max(o[3] for o in out) - min(o[2] for o in out)
+    return done, wall
+
+
+def cpu_baseline(synth, budget_s=10.0):
+    """The float64 oracle (recurrent form) on the headline prefill workload,
+    timed on this host: (b, h) pairs split over one worker process per core
+    (one BLAS thread each), and on one core alone."""
+    model, host_cores = host_identity()
+    cfg = synth.WORKLOADS[PREFILL]
+    nw = max(1, min(host_cores, CPU_WORKERS_MAX, cfg["B"] * cfg["H"]))
+    done_p, wall_p = _oracle_parallel("prefill", nw, budget_s)
+    done_1, wall_1 = _oracle_parallel("prefill", 1, budget_s)
+    H = cfg["H"]
+    return {"value": done_p / H / wall_p, "unit": "tokens/s", "cores": nw,
             "kind": "oracle",
-            "sample": (f"{done_tokens // cfg['N']} batch elements (all {cfg['H']} heads, "
-                       f"N={cfg['N']}; passes over the workload's {cfg['B']}), float64 "
-                       f"numpy recurrence, {spent:.1f} s"),
-            "host": platform.processor() or platform.machine()}
+            "sample": (f"float64 numpy recurrence over the headline workload's "
+                       f"{cfg['B'] * cfg['H']} (b,h) pairs (N={cfg['N']}) split over {nw} "
+                       f"worker processes, one BLAS thread each, passes repeated for "
+                       f"{wall_p:.1f} s: {done_p // cfg['N']} pair-sequences; tokens count "
+                       f"all {H} heads"),
+            "one_core_value": done_1 / H / wall_1,
+            "one_core_sample": f"{done_1 // cfg['N']} pair-sequences on one core, {wall_1:.1f} s",
+            "cpu_model": model, "host_cores": host_cores,
+            "label": "float64 CPU oracle vs bf16 GPU kernels: context, not like-for-like"}
 
 
 def cpu_baseline_decode(synth, budget_s=8.0):
-    """Oracle decode steps for one sequence (16 heads), the 128-step run
-    repeated until the time budget is used, scaled to 256 sequences."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    import oracle
-
+    """Oracle decode steps of the generation workload on this host: the
+    256 sequences split over worker processes (one BLAS thread each), each
+    running the 128 steps of its sequences from an unseeded state (S = 0,
+    z = 1); and the same on one core for 1 of every 16 sequences, scaled to
+    all 256."""
+    model, host_cores = host_identity()
     cfg = synth.WORKLOADS[DECODE]
-    _, _, _, sq, sk, sv = synth.workload_inputs(DECODE, seed=0, B=1)
-    D = feature_dim("taylor2", cfg["d_k"])
-    q64, k64, v64 = sq.f64(), sk.f64(), sv.f64()
-    runs = 0
-    dt = 0.0
-    with threadpool_limits(limits=1):
-        while dt < budget_s:
-            S = np.zeros((1, cfg["H"], D, cfg["d_v"]))
-            z = np.ones((1, cfg["H"], D))
-            t0 = time.perf_counter()
-            for t in range(cfg["steps"]):
-                _, S, z = oracle.decode_step(q64[:, :, t], k64[:, :, t], v64[:, :, t],
-                                             S, z, "taylor2")
-            dt += time.perf_counter() - t0
-            assert np.all(np.isfinite(S))
-            runs += 1
-    per_step_all = dt / (runs * cfg["steps"]) * cfg["B"]
-    return {"value": 1.0 / per_step_all, "unit": "steps/s", "cores": 1,
+    nw = max(1, min(host_cores, CPU_WORKERS_MAX, cfg["B"]))
+    done_p, wall_p = _oracle_parallel("decode", nw, budget_s)
+    # one core: the worker for sequences 0, 16, 32, ... of a 16-way split
+    done_1, wall_1 = _oracle_parallel_one("decode", budget_s)
+    return {"value": done_p / cfg["B"] / wall_p, "unit": "steps/s", "cores": nw,
             "kind": "oracle",
-            "sample": (f"{runs} runs of 1 of {cfg['B']} sequences x {cfg['H']} heads, "
-                       f"{cfg['steps']} steps each, {dt:.1f} s, scaled x{cfg['B']}")}
+            "sample": (f"float64 numpy decode steps, {cfg['B']} sequences x {cfg['H']} "
+                       f"heads (D=273, d_v={cfg['d_v']}) split over {nw} worker processes, "
+                       f"{cfg['steps']} steps per run, {wall_p:.1f} s"),
+            "state": "unseeded (S = 0, z = 1); the step's cost does not depend on it",
+            "one_core_value": done_1 / cfg["B"] / wall_1,
+            "one_core_sample": (f"sequences 0, 16, ..., 240 on one core, {wall_1:.1f} s, "
+                                f"scaled to {cfg['B']} sequences"),
+            "cpu_model": model, "host_cores": host_cores}
+
+
+def _oracle_parallel_one(kind, budget_s):
+    """One worker process doing 1/16 of the decode sequences alone."""
+    import multiprocessing as mp
+
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(1)
+    results = ctx.Queue()
+    p_ = ctx.Process(target=_oracle_worker,
+                     args=(kind, 0, CPU_WORKERS_MAX, budget_s, barrier, results))
+    p_.start()
+    w, done, t0, t1 = results.get(timeout=budget_s * 4 + 300)
+    p_.join()
+    return done, t1 - t0
 
 
 def main():
@@ -498,9 +606,19 @@ def main():
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    from causal_linear_attention_linattn_amd import synth
+
+    # The CPU baselines run first, in spawned worker processes, before this
+    # process touches the GPU.
+    cpu_prefill = cpu_decode = None
+    if not args.no_cpu_baseline and not args.copy_calibration and not args.only:
+        cpu_prefill = cpu_baseline(synth)
+        if not args.no_decode:
+            cpu_decode = cpu_baseline_decode(synth)
+
     import torch
 
-    from causal_linear_attention_linattn_amd import ops, synth
+    from causal_linear_attention_linattn_amd import ops
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -639,10 +757,12 @@ def main():
                 "hbm_frac": gbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "graph_ms_per_step": gms_graph,
             }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(synth)
-        if not args.no_decode:
-            out["decode"]["cpu_baseline"] = cpu_baseline_decode(synth)
+    if cpu_prefill is not None:
+        out["cpu_baseline"] = cpu_prefill
+        cpu_prefill["gpu_over_cpu"] = out["value"] / cpu_prefill["value"]
+        if cpu_decode is not None and "decode" in out:
+            cpu_decode["gpu_over_cpu"] = out["decode"]["value"] / cpu_decode["value"]
+            out["decode"]["cpu_baseline"] = cpu_decode
         out["cpu_baseline"]["claim_on_pages"] = (
             "the 'Transformers are RNNs' abstract claims linear transformers "
             "are up to 4000 times faster than softmax transformers at "

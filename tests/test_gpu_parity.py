@@ -748,15 +748,28 @@ def _sampled_rows(n, rng, count=32):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name,heads", [("layer_elu1_bf16", 6),
-                                        ("based_taylor2_bf16", 6),
-                                        ("long_elu1_bf16", 3)])
-def test_full_size_prefill(name, heads):
-    """Full-size workloads in the default launch configuration: sampled rows
-    and sampled final states against the oracle, convex hull for all rows."""
+def _default_segments(BH, N):
+    """Segment length (tokens) of the library's default plan: enough
+    segments per head for about 256 workgroups, each of at least 8 chunks
+    of 64 tokens (the plan formed in csrc/api.hip)."""
+    nchunks = -(-N // 64)
+    nseg = max(1, min(-(-256 // BH), max(1, nchunks // 8)))
+    return 64 * -(-nchunks // nseg)
+
+
+@pytest.mark.parametrize("name,rows_per_head", [("layer_elu1_bf16", 8),
+                                                ("based_taylor2_bf16", 8),
+                                                ("long_elu1_bf16", 64)])
+def test_full_size_prefill(name, rows_per_head):
+    """Full-size workloads in the default launch configuration.  Every
+    (b, h) is checked against the definition on t = 0, t = N - 1, the first
+    and last row of every segment of the default plan and random rows
+    (rows_per_head in all, at least); the final state of every head against
+    its closed form; every row against the convex hull."""
     _log(f"full-size prefill {name}")
     cfg = synth.WORKLOADS[name]
     fmap = cfg["fmap"]
+    B, H, N = cfg["B"], cfg["H"], cfg["N"]
     q, k, v = synth.workload_inputs(name, seed=0)
     y, (S, z) = gpu_prefill(q, k, v, fmap, return_state=True)
     y = ops.to_numpy64(y)
@@ -767,18 +780,20 @@ def test_full_size_prefill(name, heads):
     hi = np.maximum.accumulate(v64, axis=2)
     slack = 2e-2 * (hi - lo) + 1e-6
     assert np.all(y >= lo - slack) and np.all(y <= hi + slack)
+    del lo, hi, slack
+    seg = _default_segments(B * H, N)
+    ends = sorted({0, N - 1} | _segment_ends(0, N, seg))
     rng = np.random.default_rng(1)
-    B, H, N = cfg["B"], cfg["H"], cfg["N"]
-    bh_list = [(int(b), int(h)) for b, h in zip(rng.integers(0, B, heads),
-                                                rng.integers(0, H, heads))]
     q64, k64 = q.f64(), k.f64()
-    S = ops.to_numpy64(S)
-    for b, h in bh_list:
-        rows = _sampled_rows(N, rng)
-        ref = oracle.attention_rows(q64[b, h], k64[b, h], v64[b, h], fmap, rows)
-        assert row_err(y[b, h, rows], ref) <= TOL["bf16"], (b, h)
-        S_ref, _ = oracle.final_state(k64[b, h], v64[b, h], fmap)
-        assert state_err(S[b, h][None, None], S_ref[None, None]) <= TOL["bf16"]
+    for b in range(B):
+        for h in range(H):
+            extra = max(4, rows_per_head - len(ends))
+            rows = sorted(set(ends) | set(rng.integers(0, N, size=extra).tolist()))
+            ref = oracle.attention_rows(q64[b, h], k64[b, h], v64[b, h], fmap, rows)
+            assert row_err(y[b, h, rows], ref) <= TOL["bf16"], (b, h)
+    S_ref, z_ref = oracle.final_state(k64, v64, fmap)
+    assert state_err(ops.to_numpy64(S), S_ref) <= TOL["bf16"]
+    assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= TOL["bf16"]
 
 
 def test_full_size_gated_prefill():
