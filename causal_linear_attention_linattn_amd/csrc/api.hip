@@ -138,7 +138,7 @@ bool plan_segments(int64_t BH, int64_t N, int64_t seg_len, int64_t row_bytes,
   return true;
 }
 
-// The segment-sum pass of the Taylor maps (18 state row tiles per chunk)
+// The segment-sum pass of the Taylor maps (10 state row tiles per chunk)
 // splits each segment into `sum_split` parts when the heads are too few for
 // one workgroup per segment to occupy the GPU twice over, as long as a part
 // keeps kMinSumChunks chunks: measured on one MI355X at B=8 H=16 N=2048,

@@ -37,11 +37,19 @@
 // from its prefix.  With one segment per head only the last kernel runs.
 //
 // Feature order inside the kernels.  ELU1 uses the natural order.  TAYLOR2
-// (d_k = 16) stores the 256 pairwise features first (index 16a + b, value
-// k_a k_b without the 1/sqrt2, which is moved to the query side as 1/2),
-// then the constant (256) and the 16 linear features (257..272), then 15
-// zero pads up to 288 = 9 MFMA K blocks.  The exported states use the
-// pages' order [1, x, vec(x x^T)/sqrt2] and are converted at the boundary.
+// (d_k = 16) keeps each unordered pair of key coordinates once: k_a k_b
+// multiplies q_b k_b q_a k_a and q_a k_a q_b k_b alike, so the second-order
+// term sum_{a,b} q_a q_b k_a k_b / 2 equals sum_a q_a^2 k_a^2 / 2 +
+// sum_{a<b} q_a q_b k_a k_b, and the state needs 136 pair rows instead of
+// 256 (taylor_row: rows 0..127 hold the pairs (a, a + t mod 16), a = r / 8,
+// t = r mod 8, rows 128..135 the pairs (t, t + 8)), then the constant (136),
+// the 16 linear features (137..152) and 7 zero pads: 160 = 5 MFMA K blocks.
+// The query carries the weights (q_a^2 / 2 for a square, q_a q_b for a
+// pair).  The exported states use the pages' order [1, x, vec(x x^T)/sqrt2]
+// and are converted at the boundary: only the symmetric part of an ordered
+// pair block reaches any output, so an initial state's antisymmetric part
+// is carried to the exported state (times the total decay in the gated
+// form) without entering the walk.
 #pragma once
 
 #include "device.hpp"
@@ -49,13 +57,14 @@
 
 namespace linattn {
 
-// Waves per chunk workgroup.  The Taylor state (18 row tiles) is spread
+// Waves per chunk workgroup.  The Taylor state (10 row tiles) is spread
 // over 8 waves for bf16 inputs, so that each holds fewer accumulators and
 // two waves share a SIMD; in the output kernels waves 0-3 then make the
 // outputs and waves 4-7 own the state (the role split below).  Measured on
-// one MI355X at B=8 H=16 N=2048: 111.7 -> 106.6 us per call with every wave
-// doing both, 79.8 -> 70.7 us from the role split, and for the gated form
-// 107.2 -> 83.6 us (4 waves -> 8 split; 8 waves without the split spilled).
+// one MI355X at B=8 H=16 N=2048, with the earlier 18-tile ordered-pair
+// state: 111.7 -> 106.6 us per call with every wave doing both, 79.8 ->
+// 70.7 us from the role split, and for the gated form 107.2 -> 83.6 us
+// (4 waves -> 8 split; 8 waves without the split spilled).
 // Float tiles keep 4 waves.  The plain bf16 ELU1 segment-sum kernel at
 // d_k = 64 also runs 8 waves: its 4 state row tiles are each shared by two
 // waves that own different column tiles (the column split below), so that
@@ -99,33 +108,37 @@ struct PrefillShape : StateShape<MAP, DK, DV> {
 template <bool OUT>
 constexpr int kRing = OUT ? 2 : 4;
 
-// Internal feature row -> exported row (or -1 for padding) and the factor
-// that converts an exported value into the internal one.  Internal rows
-// 0..255 hold the ordered pairs (a, b) = (r / 16, r % 16) with key feature
-// k_a k_b, row 256 the constant and 257..272 the linear features.
-//   ordered export: pair (a, b) at 17 + 16 a + b, value internal / sqrt 2;
-//   unordered export (sym): pair {a, b} at 17 + p(min, max) with
-//     p(a, b) = a d - a (a - 1) / 2 + (b - a), value internal for a != b and
-//     internal / sqrt 2 for a == b.  Both (a, b) and (b, a) import from the
-//     same exported row; only a <= b is exported (`owner`).
-template <int MAP, int DK>
-__device__ __forceinline__ int ext_row(int r, bool sym, float& to_internal,
-                                       bool& owner) {
-  to_internal = 1.0f;
-  owner = true;
-  if (MAP == MAP_ELU1) return r < DK ? r : -1;
-  if (r < 256) {
-    if (!sym) {
-      to_internal = kSqrt2;
-      return 17 + r;
-    }
-    const int pa = r >> 4, pb = r & 15;
-    const int lo = pa < pb ? pa : pb, hi = pa < pb ? pb : pa;
-    owner = pa <= pb;
-    if (pa == pb) to_internal = kSqrt2;
-    return 17 + lo * DK - lo * (lo - 1) / 2 + (hi - lo);
+// Internal Taylor rows.  The key features k_a k_b of the pair (a, b) and
+// of (b, a) are equal, so the state keeps each unordered pair once (the
+// query side carries q_a q_b, or q_a^2 / 2 for a square, so that
+// phi(q).phi(k) = 1 + q.k + (q.k)^2 / 2 holds):
+//   r < 128:         pair (a, b), a = r / 8, b = (a + r % 8) mod 16: the 8
+//                    coordinates that follow a circularly (a itself first),
+//                    so every pair at circular distance 0..7 appears once;
+//   128 <= r < 136:  pair (r - 128, r - 120), the pairs at distance 8;
+//   136:             the constant feature;  137 .. 152: the linear ones;
+//   153 .. 159:      zero padding (10 row tiles, 5 MFMA K blocks).
+// Returns the kind of row r: 0 pair (a, b set), 1 constant, 2 linear (a
+// set to the coordinate), 3 padding.
+__device__ __forceinline__ int taylor_row(int r, int& a, int& b) {
+  a = 0;
+  b = 0;
+  if (r < 128) {
+    a = r >> 3;
+    b = (a + (r & 7)) & 15;
+    return 0;
   }
-  return r < 273 ? r - 256 : -1;
+  if (r < 136) {
+    a = r - 128;
+    b = r - 120;
+    return 0;
+  }
+  if (r == 136) return 1;
+  if (r < 153) {
+    a = r - 137;
+    return 2;
+  }
+  return 3;
 }
 
 // Exported feature rows of a head's state.
@@ -134,54 +147,119 @@ __device__ __forceinline__ int ext_rows(bool sym) {
   return MAP == MAP_TAYLOR2 && sym ? kSymD<DK> : StateShape<MAP, DK, DV>::D;
 }
 
+// Exported rows of the Taylor maps: ordered pair (a, b) at 17 + 16 a + b;
+// unordered pair {a, b}, a <= b, at 17 + a d - a (a - 1) / 2 + (b - a).
+__device__ __forceinline__ int ordered_pair_row(int a, int b) { return 17 + 16 * a + b; }
+__device__ __forceinline__ int sym_pair_row(int a, int b) {
+  const int lo = a < b ? a : b, hi = a < b ? b : a;
+  return 17 + lo * 16 - lo * (lo - 1) / 2 + (hi - lo);
+}
+
+// One column (col < DV: S, col == DV: z) of the exported layout of
+// sequence bh, as a row accessor.
+struct ExtCol {
+  const float* S;
+  const float* z;
+  int D, DV, bh, col;
+  __device__ __forceinline__ float at(int e) const {
+    return col < DV ? S[((size_t)bh * D + e) * DV + col] : z[(size_t)bh * D + e];
+  }
+};
+
 // One lane's 4 values of state tile (rt, ct) read from the exported
 // layout S [D, DV], z [D] of sequence bh, converted to the internal one.
+// Taylor pair rows take the pair's symmetric part: the ordered layout's
+// (a, b) and (b, a) rows are added (their antisymmetric part contributes
+// nothing to any output: q^T A q = 0 for antisymmetric A; the export
+// carries it over, state_out_tile).
 template <int MAP, int DK, int DV>
 __device__ __forceinline__ f32x4_t state_in_tile(const float* S_in,
                                                  const float* z_in, bool sym,
                                                  int bh, int rt, int ct,
                                                  int lane) {
-  const int D = ext_rows<MAP, DK, DV>(sym);
-  f32x4_t r;
   const int col = 16 * ct + (lane & 15);
+  const ExtCol in{S_in, z_in, ext_rows<MAP, DK, DV>(sym), DV, bh, col};
+  f32x4_t r;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int row = 16 * rt + 4 * (lane >> 4) + t;
-    float f;
-    bool owner;
-    const int e = ext_row<MAP, DK>(row, sym, f, owner);
     float val = 0.0f;
-    if (e >= 0) {
-      if (col < DV)
-        val = S_in[((size_t)bh * D + e) * DV + col];
-      else if (col == DV)
-        val = z_in[(size_t)bh * D + e];
+    if (col <= DV) {
+      if constexpr (MAP == MAP_ELU1) {
+        if (row < DK) val = in.at(row);
+      } else {
+        int a, b;
+        const int kind = taylor_row(row, a, b);
+        if (kind == 0) {
+          if (sym)
+            val = in.at(sym_pair_row(a, b)) * (a == b ? kSqrt2 : 1.0f);
+          else if (a == b)
+            val = in.at(ordered_pair_row(a, a)) * kSqrt2;
+          else
+            val = (in.at(ordered_pair_row(a, b)) + in.at(ordered_pair_row(b, a))) * kInvSqrt2;
+        } else if (kind == 1) {
+          val = in.at(0);
+        } else if (kind == 2) {
+          val = in.at(1 + a);
+        }
+      }
     }
-    r[t] = val * f;
+    r[t] = val;
   }
   return r;
 }
 
+// Export of one lane's 4 values of state tile (rt, ct).  An ordered Taylor
+// pair (a != b) is written to both (a, b) and (b, a); when the call started
+// from an ordered S_in, whose pair rows need not agree, their
+// antisymmetric part (S_in(a,b) - S_in(b,a)) / 2 is carried over, scaled by
+// anti_scale (1, or the gated form's total decay).  In place (S_out is
+// S_in) the lane reads both rows before it writes them.
 template <int MAP, int DK, int DV>
 __device__ __forceinline__ void state_out_tile(float* S_out, float* z_out,
                                                bool sym, int bh, int rt,
                                                int ct, int lane,
-                                               const f32x4_t& v) {
+                                               const f32x4_t& v,
+                                               const float* S_in = nullptr,
+                                               const float* z_in = nullptr,
+                                               float anti_scale = 1.0f) {
   const int D = ext_rows<MAP, DK, DV>(sym);
   const int col = 16 * ct + (lane & 15);
   if (col > DV) return;
+  float* out = col < DV ? S_out : z_out;
+  auto addr = [&](int e) -> size_t {
+    return col < DV ? ((size_t)bh * D + e) * DV + col : (size_t)bh * D + e;
+  };
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int row = 16 * rt + 4 * (lane >> 4) + t;
-    float f;
-    bool owner;
-    const int e = ext_row<MAP, DK>(row, sym, f, owner);
-    if (e < 0 || !owner) continue;
-    const float val = v[t] / f;
-    if (col < DV)
-      S_out[((size_t)bh * D + e) * DV + col] = val;
-    else
-      z_out[(size_t)bh * D + e] = val;
+    if constexpr (MAP == MAP_ELU1) {
+      if (row < DK) out[addr(row)] = v[t];
+    } else {
+      int a, b;
+      const int kind = taylor_row(row, a, b);
+      if (kind == 0) {
+        if (sym) {
+          out[addr(sym_pair_row(a, b))] = v[t] * (a == b ? kInvSqrt2 : 1.0f);
+        } else if (a == b) {
+          out[addr(ordered_pair_row(a, a))] = v[t] * kInvSqrt2;
+        } else {
+          float anti = 0.0f;
+          if (S_in != nullptr) {
+            const ExtCol in{S_in, z_in, D, DV, bh, col};
+            anti = 0.5f * (in.at(ordered_pair_row(a, b)) - in.at(ordered_pair_row(b, a))) *
+                   anti_scale;
+          }
+          const float base = v[t] * kInvSqrt2;
+          out[addr(ordered_pair_row(a, b))] = base + anti;
+          out[addr(ordered_pair_row(b, a))] = base - anti;
+        }
+      } else if (kind == 1) {
+        out[addr(0)] = v[t];
+      } else if (kind == 2) {
+        out[addr(1 + a)] = v[t];
+      }
+    }
   }
 }
 
@@ -459,8 +537,9 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void ch
   // ------------------------------------------------------------ roles ----
   // The 8-wave Taylor output kernels run two specialised walks side by
   // side: waves 0-3 make the chunk's outputs and own no state; waves 4-7 own
-  // every state row tile (tiles w-4, w, w+4, w+8 of the pair features, then
-  // the constant/linear tiles 16 and 17 on waves 4 and 5).  The 8-wave ELU1
+  // every state row tile (tiles w-4 and w of the pair features, then tiles
+  // 8 and 9, the distance-8 pairs, the constant and the linear features, on
+  // waves 4 and 5).  The 8-wave ELU1
   // segment-sum kernel runs two column halves: waves w and w+4 share row
   // tile w & 3, wave w owning its first column tiles and wave w+4 the rest.
   // Each walk is straight-line code with registers of its own, and all pass
@@ -472,7 +551,7 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void ch
     constexpr int ROLE = decltype(role_c)::value;
     const bool qwave_r = ROLE == 1;
     constexpr int kMT = ROLE == 1 || ROLE >= 3 ? 1 : (SH::NRT + 3) / 4;
-    static_assert(ROLE >= 3 || (MAP != MAP_ELU1 && SH::NRT == 18), "the split owns 16 + 2 tiles");
+    static_assert(ROLE >= 3 || (MAP != MAP_ELU1 && SH::NRT == 10), "the split owns 8 + 2 tiles");
     static_assert(ROLE < 3 || (!OUT && SH::NRT == 4), "the column split pairs waves w, w + 4");
     // state row tile m of this wave (a tile index >= NRT means none)
     auto row_tile = [&](int m) __attribute__((always_inline)) -> int {

@@ -61,7 +61,11 @@ struct StateShape {
   static constexpr int D = MAP == MAP_ELU1      ? DK
                            : MAP == MAP_TAYLOR2 ? 1 + DK + DK * DK
                                                 : kSymD<DK>;
-  static constexpr int DP = MAP == MAP_ELU1 ? ((DK + 31) / 32) * 32 : 288;
+  // rows of the state inside the prefill kernels: ELU1 d_k rounded up to a
+  // 32-row MFMA K block; the Taylor maps keep each unordered pair of key
+  // coordinates once (136 pairs, the constant, 16 linear features, padding:
+  // 160 rows; prefill_impl.hpp, taylor_row)
+  static constexpr int DP = MAP == MAP_ELU1 ? ((DK + 31) / 32) * 32 : 160;
   static constexpr int NRT = DP / 16;    // 16-row tiles of S'
   static constexpr int NKB = DP / 32;    // 32-wide K blocks over features
   static constexpr int NCT = DV / 16 + 1;  // column tiles of S' incl. z

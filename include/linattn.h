@@ -171,7 +171,7 @@ linattn_status_t linattn_prefill(int map, int dtype, int64_t B, int64_t H,
  *   Returns LINATTN_ERR_SCRATCH, before anything is launched, when
  *   linattn_prefill_workspace_bytes(map, dtype, B, H, N, d_k, d_v, seg_len)
  *   exceeds LINATTN_NOALLOC_SCRATCH_BYTES (a Taylor part sum at d_v = 64
- *   takes 92,160 bytes per head and part, so B=8 H=16 N=2048 needs 47 MB;
+ *   takes 51,200 bytes per head and part, so B=8 H=16 N=2048 needs 26 MB;
  *   ELU1 at d = 64 takes 20,480); other errors as linattn_prefill.
  *   All calls on one device share its array: two calls that may run at the
  *   same time on one device (different streams, no ordering between them)

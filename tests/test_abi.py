@@ -102,11 +102,11 @@ def test_workspace_bytes(lib):
     # With few heads the Taylor segment-sum pass splits each segment in two
     # (B*H*(nseg-1) below 512 workgroups and halves of >= 4 chunks),
     # doubling the slots; ELU1 never splits.
-    slot_tay = 18 * 5 * 256
+    slot_tay = 10 * 5 * 256
     # 512 heads x 3 summed segments fill the GPU already: no split
     assert f(1, 1, 64, 8, 2048, 16, 64, 512) == 512 * 4 * slot_tay * 4 + logs(512 * 4)
     # 6-chunk segments would leave 3-chunk halves: no split
-    assert f(1, 1, 1, 2, 4096, 16, 16, 384) == 2 * 11 * (18 * 2 * 256) * 4 + logs(2 * 11)
+    assert f(1, 1, 1, 2, 4096, 16, 16, 384) == 2 * 11 * (10 * 2 * 256) * 4 + logs(2 * 11)
     assert f(1, 1, 8, 16, 2048, 16, 64, 512) == 128 * 8 * slot_tay * 4 + logs(128 * 8)
     # the unordered-pair map runs on the same kernels and workspace
     assert f(2, 1, 8, 16, 2048, 16, 64, 512) == 128 * 8 * slot_tay * 4 + logs(128 * 8)
@@ -339,7 +339,7 @@ def test_binding_rejects_mis_sized_buffers_before_the_library(lib):
 def test_noalloc_rejects_calls_beyond_its_fixed_scratch(lib):
     """linattn_prefill_noalloc refuses, before any HIP call, a plan whose part
     sums exceed its fixed array: Taylor d_v = 64 at 128 heads in 128 segments
-    of one chunk needs 128 * 128 * 92160 bytes."""
+    of one chunk needs 128 * 128 * 51200 bytes."""
     need = lib.linattn_prefill_workspace_bytes(1, 1, 8, 16, 8192, 16, 64, 64)
     assert need > 64 << 20
     rc = lib.linattn_prefill_noalloc(
