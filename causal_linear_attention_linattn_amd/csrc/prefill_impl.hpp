@@ -141,6 +141,26 @@ __device__ __forceinline__ int taylor_row(int r, int& a, int& b) {
   return 3;
 }
 
+// Rows of the transposed key tile (k_0 .. k_15, then a row of ones and a
+// row of zeros) whose product is lane i16's key feature in state row tile
+// rt: internal row 16 rt + i16 (taylor_row) is sKT[pa] * sKT[pb], so that
+// the pairs, the constant (ones x ones), the linear features (k_a x ones)
+// and the padding (zeros x ones) all take the same two reads and one
+// product.  Tiles past the last (unused accumulators) read zeros.
+constexpr int kKtOnes = 16, kKtZeros = 17;
+__device__ __forceinline__ void taylor_kt_rows(int rt, int i16, int& pa, int& pb) {
+  if (rt < 8) {
+    pa = 2 * rt + (i16 >> 3);
+    pb = (pa + (i16 & 7)) & 15;
+  } else if (rt == 8) {
+    pa = i16 < 8 ? i16 : (i16 == 8 ? kKtOnes : i16 - 9);
+    pb = i16 < 8 ? i16 + 8 : kKtOnes;
+  } else {
+    pa = rt == 9 && i16 <= 8 ? i16 + 7 : kKtZeros;
+    pb = kKtOnes;
+  }
+}
+
 // Exported feature rows of a head's state.
 template <int MAP, int DK, int DV>
 __device__ __forceinline__ int ext_rows(bool sym) {
@@ -467,13 +487,14 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void ch
 
   // sK: rows of phi(K) (ELU1) or k (TAYLOR2); needed by the output kernel
   // for the scores and, for bf16 ELU1, by both kernels as the transposed
-  // source of phi(K)^T.  sKT: K transposed (float, and TAYLOR2).  sS: the
+  // source of phi(K)^T.  sKT: K transposed (float, and TAYLOR2; TAYLOR2
+  // appends a row of ones and a row of zeros, taylor_kt_rows).  sS: the
   // state S'^T in the MFMA operand precision, column-major; two copies
   // unless that does not fit next to the tiles (float TAYLOR2).
   constexpr bool kNeedK = OUT || (BF && MAP == MAP_ELU1);
   constexpr bool kNeedKT = !(BF && MAP == MAP_ELU1);
   constexpr int K_EL = kNeedK ? (BF ? C * RTK::STRIDE : C * KS) : EPU;
-  constexpr int KT_EL = kNeedKT ? DK * CS : EPU;
+  constexpr int KT_EL = kNeedKT ? (MAP == MAP_ELU1 ? DK : DK + 2) * CS : EPU;
   constexpr int V_EL = BF ? C * RTV::STRIDE : DV * CS;
   constexpr int S_EL = OUT ? SH::NCOL * PS : EPU;
   constexpr int kTileBytes = 2 * (K_EL + KT_EL + V_EL) * (int)sizeof(T) + (GATED ? 2 * C * 16 : 0);
