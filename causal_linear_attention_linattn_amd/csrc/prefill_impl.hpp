@@ -487,22 +487,27 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void ch
 
   // sK: rows of phi(K) (ELU1) or k (TAYLOR2); needed by the output kernel
   // for the scores and, for bf16 ELU1, by both kernels as the transposed
-  // source of phi(K)^T.  sKT: K transposed (float, and TAYLOR2; TAYLOR2
-  // appends a row of ones and a row of zeros, taylor_kt_rows).  sS: the
+  // source of phi(K)^T.  sKT: K transposed (float, and TAYLOR2, where it is
+  // fp32 for every input type so that the key products read it without
+  // unpacking, with a row of ones and a row of zeros appended,
+  // taylor_kt_rows; row stride KCS).  sS: the
   // state S'^T in the MFMA operand precision, column-major; two copies
   // unless that does not fit next to the tiles (float TAYLOR2).
   constexpr bool kNeedK = OUT || (BF && MAP == MAP_ELU1);
   constexpr bool kNeedKT = !(BF && MAP == MAP_ELU1);
   constexpr int K_EL = kNeedK ? (BF ? C * RTK::STRIDE : C * KS) : EPU;
-  constexpr int KT_EL = kNeedKT ? (MAP == MAP_ELU1 ? DK : DK + 2) * CS : EPU;
+  using KTT = std::conditional_t<MAP == MAP_TAYLOR2, float, T>;
+  constexpr int KCS = C + 16 / (int)sizeof(KTT);  // padded by 16 bytes
+  constexpr int KT_EL = kNeedKT ? (MAP == MAP_ELU1 ? DK : DK + 2) * KCS : 4;
   constexpr int V_EL = BF ? C * RTV::STRIDE : DV * CS;
   constexpr int S_EL = OUT ? SH::NCOL * PS : EPU;
-  constexpr int kTileBytes = 2 * (K_EL + KT_EL + V_EL) * (int)sizeof(T) + (GATED ? 2 * C * 16 : 0);
+  constexpr int kTileBytes = 2 * ((K_EL + V_EL) * (int)sizeof(T) + KT_EL * (int)sizeof(KTT)) +
+                             (GATED ? 2 * C * 16 : 0);
   constexpr int NSB = kTileBytes + 2 * S_EL * (int)sizeof(T) <= 160 * 1024 ? 2 : 1;
   __shared__ __align__(16) T sK0[K_EL];
   __shared__ __align__(16) T sK1[K_EL];
-  __shared__ __align__(16) T sKT0[KT_EL];
-  __shared__ __align__(16) T sKT1[KT_EL];
+  __shared__ __align__(16) KTT sKT0[KT_EL];
+  __shared__ __align__(16) KTT sKT1[KT_EL];
   __shared__ __align__(16) T sV0[V_EL];
   __shared__ __align__(16) T sV1[V_EL];
   __shared__ __align__(16) T sS0[S_EL];
