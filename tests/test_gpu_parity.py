@@ -487,6 +487,60 @@ def test_prefill_in_place_many_segments(fmap, d_k, d_v, B, H, gated):
     assert state_err(z[..., None], z_ref[..., None]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("seg_len", [0, 64])
+def test_prefill_in_place_from_arbitrary_ordered_state(gated, seg_len):
+    """In place (S_out is S_in) from a random ordered Taylor state whose rows
+    (a, b) and (b, a) differ: the kernels walk only the symmetric part of the
+    pair block, and the export adds the antisymmetric part back (decayed, in
+    the gated form) from the same S_in it overwrites.  One segment and five
+    (the scanned path that aliasing takes), 32 heads; all outputs and the
+    final state against the oracle's recurrence from that state."""
+    fmap, d_k, d_v, B, H, N = "taylor2", 16, 64, 4, 8, 300
+    _log(f"prefill in place from an arbitrary ordered state gated={gated} seg_len={seg_len}")
+    scale = _qk_scale(fmap)
+    q0, k0, v0 = synth.draw_qkv(B, H, 100, d_k, d_v, seed=31, dtype="f32", qk_scale=scale)
+    z_in = oracle.attention_recurrent(q0.f64(), k0.f64(), v0.f64(), fmap)[2]
+    D = oracle.feature_dim(fmap, d_k)
+    S_in = np.random.default_rng(32).standard_normal((B, H, D, d_v)) * 4.0
+    S32, z32 = S_in.astype(np.float32), z_in.astype(np.float32)
+    q, k, v = synth.draw_qkv(B, H, N, d_k, d_v, seed=33, dtype="bf16", qk_scale=scale)
+    a = synth.draw_gate(B, H, N, seed=33, lo=0.99) if gated else None
+    if gated:
+        y_ref, S_ref, z_ref = oracle.attention_gated_recurrent(
+            q.f64(), k.f64(), v.f64(), a.astype(np.float64), fmap,
+            S0=S32.astype(np.float64), z0=z32.astype(np.float64))
+    else:
+        y_ref, S_ref, z_ref = oracle.attention_recurrent(
+            q.f64(), k.f64(), v.f64(), fmap, S0=S32.astype(np.float64),
+            z0=z32.astype(np.float64))
+    S = torch.from_numpy(S32).to(DEV)
+    z = torch.from_numpy(z32).to(DEV)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    y = torch.empty_like(vd)
+    nws = ops.workspace_bytes(fmap, torch.bfloat16, B, H, N, d_k, d_v, seg_len)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+    L = ops.load_library()
+    m = ops.MAPS[fmap]
+    if gated:
+        ad = _gate_dev(a)
+        rc = L.linattn_prefill_gated(m, 1, B, H, N, d_k, d_v, ops._ptr(qd), ops._ptr(kd),
+                                     ops._ptr(vd), ops._ptr(ad), 1, ops._ptr(y),
+                                     ops._ptr(S), ops._ptr(z), ops._ptr(S), ops._ptr(z),
+                                     seg_len, ops._ptr(ws), nws, ops._stream(qd))
+    else:
+        rc = L.linattn_prefill(m, 1, B, H, N, d_k, d_v, ops._ptr(qd), ops._ptr(kd),
+                               ops._ptr(vd), ops._ptr(y), ops._ptr(S), ops._ptr(z),
+                               ops._ptr(S), ops._ptr(z), seg_len, ops._ptr(ws), nws,
+                               ops._stream(qd))
+    assert rc == 0
+    torch.cuda.synchronize()
+    tol = TOL["bf16"]
+    assert row_err(ops.to_numpy64(y), y_ref) <= tol
+    assert state_err(ops.to_numpy64(S), S_ref) <= tol
+    assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
+
+
 # ------------------------------------------------------- gated form ------
 def _gate_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
