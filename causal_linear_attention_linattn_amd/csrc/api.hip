@@ -154,6 +154,19 @@ int sum_split(int map, int64_t BH, int nseg, int seg_chunks) {
   return 2;
 }
 
+// Chunks of segment 0 in a prefix_mode 3 plan (two segments), a multiple
+// of two (the output walk takes two chunks per trip), at least 2 and leaving
+// segment 1 at least one chunk.  The share evens out the two workgroups of a
+// head: measured on one MI355X at B=8 H=16 N=2048 d_v=64 (32 chunks), bf16
+// 20 / 22 / 24 chunks 37.2 / 36.6 / 38.5 us (gated 46.7 / 45.1 / 47.6 us),
+// float 18 / 20 / 22 chunks 222 / 210 / 227 us.
+int64_t self_prefix_seg0_chunks(int64_t nchunks, int dtype) {
+  const int64_t num = dtype == LINATTN_DTYPE_F32 ? 10 : 11;
+  int64_t c0 = (nchunks * num / 16) & ~(int64_t)1;
+  if (c0 >= nchunks) c0 = (nchunks - 1) & ~(int64_t)1;
+  return c0 < 2 ? 2 : c0;
+}
+
 // Workspace: BH * nseg * sum_split slots of partial states, then one float
 // per slot (the log2 decay of a part in gated calls), padded to 16 bytes.
 size_t slots_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nslot) {
@@ -335,6 +348,20 @@ linattn_status_t prefill_common(int map, int dtype, int64_t B, int64_t H,
                  ? a.ws + slots_bytes(map, BH, d_k, d_v, a.nslot) / sizeof(float)
                  : nullptr;
   a.normalize = gated ? normalize : 1;
+  // Taylor maps at two segments per head (the default plan for 128 to 255
+  // heads): no segment-sum pass.  The workgroup of segment 1 walks segment
+  // 0 itself first, advancing the state without outputs (prefix_mode 3), so
+  // the call is one launch and reads no workspace.  Segment 0 takes the
+  // larger share of the chunks, since such a chunk costs less than one with
+  // outputs.
+  const int64_t nchunks = (N + kChunk - 1) / kChunk;
+  if (prefill_map(map) == MAP_TAYLOR2 && seg_len == 0 && nseg == 2 && !in_place &&
+      nchunks <= kMaxSegBytes / (kChunk * row_bytes)) {
+    a.prefix_mode = 3;
+    a.seg_chunks = (int)self_prefix_seg0_chunks(nchunks, dtype);
+    a.sum_split = 1;
+    a.ws_log = nullptr;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = gated ? dispatch_prefill<true>(map, dtype, d_k, d_v, a, st)
                              : dispatch_prefill<false>(map, dtype, d_k, d_v, a, st);

@@ -498,7 +498,9 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int MAP, typename T, int DK, int DV, bool OUT, bool GATED>
+// PRE: the prefix_mode 3 output kernel (TAYLOR2 only), a separate
+// instantiation so that the other plans keep their own compiled walk.
+template <int MAP, typename T, int DK, int DV, bool OUT, bool GATED, bool PRE = false>
 __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void chunk_kernel(PrefillArgs a) {
   using SH = PrefillShape<MAP, T, DK, DV, kChunkWaves<MAP, T, DK, GATED, OUT>>;
   using E = Elem<T>;
@@ -572,8 +574,21 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void ch
   const int bh = blockIdx.x / nseg_here;
   const int seg = blockIdx.x % nseg_here;
   const int64_t N = a.N;
-  const int64_t tok_begin = (int64_t)seg * seg_chunks * C;
+  int64_t tok_begin = (int64_t)seg * seg_chunks * C;
   int64_t tok_end = tok_begin + (int64_t)seg_chunks * C;
+  // TAYLOR2, prefix_mode 3 (two segments, no segment-sum pass; the PRE
+  // kernel): both workgroups of a head walk from token 0.  Segment 0 covers
+  // the first seg_chunks chunks; segment 1 walks those chunks first as a
+  // pre-pass that only advances the state (chunks before c_out), then makes
+  // the outputs of the rest of the sequence.
+  constexpr bool kPrePass = PRE;
+  static_assert(!PRE || (OUT && MAP == MAP_TAYLOR2), "the pre-pass kernel");
+  int c_out = 0;
+  if constexpr (kPrePass) {
+    c_out = seg * seg_chunks;
+    tok_begin = 0;
+    tok_end = seg == 0 ? (int64_t)seg_chunks * C : N;
+  }
   if (tok_end > N) tok_end = N;
   const int ntok = (int)(tok_end - tok_begin);   // tokens in this segment
   const int nchunks = (ntok + C - 1) / C;
@@ -720,13 +735,20 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   using SS = StateShape<MAP, DK, DV>;
   constexpr int NT = 64 * kChunkWaves<MAP, T, DK, GATED, true>;
   constexpr int NT_SUM = 64 * kChunkWaves<MAP, T, DK, GATED, false>;
-  if (a.nseg > 1) {
+  if (a.nseg > 1 && a.prefix_mode != 3) {
     hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, false, GATED>),
                        dim3(a.BH * (a.nseg - 1) * a.sum_split), dim3(NT_SUM), 0, st, a);
     if (a.prefix_mode == 2) {
       hipLaunchKernelGGL((seg_scan_kernel<MAP, DK, DV>),
                          dim3((unsigned)(a.BH * (SS::SLOT / 4 / kScanCols))), dim3(256), 0,
                          st, a);
+    }
+  }
+  if constexpr (MAP == MAP_TAYLOR2) {
+    if (a.prefix_mode == 3) {
+      hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, true, GATED, true>),
+                         dim3(a.BH * a.nseg), dim3(NT), 0, st, a);
+      return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, true, GATED>),

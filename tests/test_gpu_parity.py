@@ -231,6 +231,48 @@ def test_prefill_gated_from_arbitrary_state(fmap, d_k, d_v, dtype, seg_len):
     assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
 
 
+@pytest.mark.parametrize("fmap,d_k,d_v", [("taylor2", 16, 64), ("taylor2sym", 16, 32)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("with_state", [False, True])
+@pytest.mark.parametrize("N", [1024, 1400])
+def test_prefill_two_segments_pre_pass(fmap, d_k, d_v, dtype, gated, with_state, N):
+    """Two default segments per head (16 and 22 chunks over 3 heads) take
+    the Taylor plan without a segment-sum pass: the workgroup of segment 1
+    walks segment 0 first without outputs.  Outputs and the exported state
+    follow the recurrence, from zero or from an arbitrary state, plain or
+    gated, with a ragged last chunk at N = 1400."""
+    _log(f"two-segment pre-pass plan {fmap} {dtype} gated={gated} state={with_state} N={N}")
+    scale = _qk_scale(fmap)
+    B, H = 1, 3
+    q, k, v = synth.draw_qkv(B, H, N, d_k, d_v, seed=N + 7, dtype=dtype, qk_scale=scale)
+    S0 = z0 = st = None
+    if with_state:
+        q0, k0, v0 = synth.draw_qkv(B, H, 100, d_k, d_v, seed=31, dtype="f32", qk_scale=scale)
+        z_in = oracle.attention_recurrent(q0.f64(), k0.f64(), v0.f64(), fmap)[2]
+        D = oracle.feature_dim(fmap, d_k)
+        S_in = np.random.default_rng(32).standard_normal((B, H, D, d_v)) * 4.0
+        S32, z32 = S_in.astype(np.float32), z_in.astype(np.float32)
+        S0, z0 = S32.astype(np.float64), z32.astype(np.float64)
+        st = (torch.from_numpy(S32).to(DEV), torch.from_numpy(z32).to(DEV))
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    if gated:
+        a = synth.draw_gate(B, H, N, seed=N, lo=0.995)
+        y_ref, S_ref, z_ref = oracle.attention_gated_recurrent(
+            q.f64(), k.f64(), v.f64(), a.astype(np.float64), fmap, S0=S0, z0=z0)
+        y, (S, z) = ops.prefill_gated(qd, kd, vd, _gate_dev(a), fmap, state=st,
+                                      return_state=True)
+    else:
+        y_ref, S_ref, z_ref = oracle.attention_recurrent(q.f64(), k.f64(), v.f64(), fmap,
+                                                         S0=S0, z0=z0)
+        y, (S, z) = ops.prefill(qd, kd, vd, fmap, state=st, return_state=True)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert row_err(ops.to_numpy64(y), y_ref) <= tol
+    assert state_err(ops.to_numpy64(S), S_ref) <= tol
+    assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
+
+
 @pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64)])
 def test_prefill_deterministic_and_segment_invariant(fmap, d_k, d_v):
     _log(f"determinism / segment invariance {fmap}")
