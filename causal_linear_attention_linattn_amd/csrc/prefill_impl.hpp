@@ -571,8 +571,15 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void ch
   // every segment but the last (sum_split parts per segment).
   const int nseg_here = OUT ? a.nseg : (a.nseg - 1) * a.sum_split;
   const int seg_chunks = OUT ? a.seg_chunks : a.seg_chunks / a.sum_split;
-  const int bh = blockIdx.x / nseg_here;
-  const int seg = blockIdx.x % nseg_here;
+  // The PRE kernel places the two workgroups of a head on one XCD (the
+  // hardware deals workgroup x + 8 r to XCD x) when the heads fill whole
+  // groups of 8: head x + 8 (r / 2), segment r % 2.  Segment 1's pre-pass
+  // reads segment 0's k and v shortly before segment 0's workgroup does, so
+  // most of those second reads hit that XCD's L2.
+  const bool same_xcd = PRE && (a.BH % 8) == 0;
+  const int bh = same_xcd ? (int)(blockIdx.x % 8 + 8 * (blockIdx.x / 16))
+                          : (int)(blockIdx.x / nseg_here);
+  const int seg = same_xcd ? (int)((blockIdx.x / 8) % 2) : (int)(blockIdx.x % nseg_here);
   const int64_t N = a.N;
   int64_t tok_begin = (int64_t)seg * seg_chunks * C;
   int64_t tok_end = tok_begin + (int64_t)seg_chunks * C;

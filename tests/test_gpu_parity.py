@@ -236,15 +236,16 @@ def test_prefill_gated_from_arbitrary_state(fmap, d_k, d_v, dtype, seg_len):
 @pytest.mark.parametrize("gated", [False, True])
 @pytest.mark.parametrize("with_state", [False, True])
 @pytest.mark.parametrize("N", [1024, 1400])
-def test_prefill_two_segments_pre_pass(fmap, d_k, d_v, dtype, gated, with_state, N):
-    """Two default segments per head (16 and 22 chunks over 3 heads) take
-    the Taylor plan without a segment-sum pass: the workgroup of segment 1
-    walks segment 0 first without outputs.  Outputs and the exported state
-    follow the recurrence, from zero or from an arbitrary state, plain or
-    gated, with a ragged last chunk at N = 1400."""
-    _log(f"two-segment pre-pass plan {fmap} {dtype} gated={gated} state={with_state} N={N}")
+@pytest.mark.parametrize("B,H", [(1, 3), (2, 8)])
+def test_prefill_two_segments_pre_pass(fmap, d_k, d_v, dtype, gated, with_state, N, B, H):
+    """Two default segments per head (16 and 22 chunks) take the Taylor
+    plan without a segment-sum pass: the workgroup of segment 1 walks
+    segment 0 first without outputs.  Outputs and the exported state follow
+    the recurrence, from zero or from an arbitrary state, plain or gated,
+    with a ragged last chunk at N = 1400.  At 16 heads (a multiple of 8)
+    the two workgroups of a head are placed on one XCD."""
+    _log(f"two-segment pre-pass plan {fmap} {dtype} gated={gated} state={with_state} N={N} B={B} H={H}")
     scale = _qk_scale(fmap)
-    B, H = 1, 3
     q, k, v = synth.draw_qkv(B, H, N, d_k, d_v, seed=N + 7, dtype=dtype, qk_scale=scale)
     S0 = z0 = st = None
     if with_state:
