@@ -387,21 +387,25 @@ def test_decode_graph_replays_match_eager(fmap, d_k, d_v):
         assert torch.equal(S_g, S_e) and torch.equal(z_g, z_e), r
 
 
-@pytest.mark.parametrize("case", ["one_segment", "part_sums", "scan", "taylor_state", "gated",
+@pytest.mark.parametrize("case", ["one_segment", "part_sums", "scan", "taylor_state",
+                                  "taylor_pre_pass", "gated_taylor_pre_pass", "gated",
                                   "sliding_window"])
 def test_prefill_graph_replays_match_eager(case):
     """Prefill calls captured in one HIP graph: every replay (other eager work
     in between) gives bit-identical outputs and final states to the same
     calls run eagerly.  The cases cover one segment per head, output
     workgroups adding their predecessors' part sums, the scan kernel, the
-    Taylor state export, the gated form, and the sliding-window prefill with
-    a generation step (its caches restored by an eager copy before each
-    replay)."""
+    Taylor state export, the Taylor two-segment plan without a segment-sum
+    pass (plain and gated), the gated form, and the sliding-window prefill
+    with a generation step (its caches restored by an eager copy before
+    each replay)."""
     _log(f"prefill graph replays {case}")
     fmap, d_k, d_v, N, seg = {"one_segment": ("elu1", 64, 64, 300, 0),
                               "part_sums": ("elu1", 64, 64, 1000, 192),
                               "scan": ("elu1", 64, 64, 1000, 64),
                               "taylor_state": ("taylor2", 16, 64, 700, 64),
+                              "taylor_pre_pass": ("taylor2", 16, 64, 1024, 0),
+                              "gated_taylor_pre_pass": ("taylor2", 16, 64, 1024, 0),
                               "gated": ("elu1", 64, 64, 1000, 64),
                               "sliding_window": ("elu1", 64, 64, 700, 0)}[case]
     q, k, v = synth.draw_qkv(2, 3, N, d_k, d_v, seed=41, dtype="bf16", qk_scale=_qk_scale(fmap))
@@ -418,7 +422,7 @@ def test_prefill_graph_replays_match_eager(case):
             kc2, vc2 = caches if caches is not None else (kc, vc)
             yd = ops.swa_decode_step(qs, ks, vs, pos, kc2, vc2, w)
             return [y, yd, kc2, vc2]
-        if case == "gated":
+        if case.startswith("gated"):
             y, (S, z) = ops.prefill_gated(qd, kd, vd, ad, fmap, return_state=True, seg_len=seg)
             return [y, S, z]
         y, (S, z) = ops.prefill(qd, kd, vd, fmap, return_state=True, seg_len=seg)
