@@ -35,6 +35,9 @@
 // state, seg_scan_kernel turns those sums into exclusive prefixes (plus the
 // optional initial state), and chunk_kernel<OUT = true> starts each segment
 // from its prefix.  With one segment per head only the last kernel runs.
+// The Taylor maps at two segments per head run one kernel instead
+// (chunk_kernel<..., PRE = true>): the workgroup of segment 1 walks segment
+// 0 first, advancing the state without outputs.
 //
 // Feature order inside the kernels.  ELU1 uses the natural order.  TAYLOR2
 // (d_k = 16) keeps each unordered pair of key coordinates once: k_a k_b
