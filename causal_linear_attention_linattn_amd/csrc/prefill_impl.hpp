@@ -89,7 +89,11 @@ struct PrefillShape : StateShape<MAP, DK, DV> {
   static constexpr int EPU = Elem<T>::kPer16B;
   static constexpr int KS = DK + EPU;       // LDS row strides (elements),
   static constexpr int CS = C + EPU;        // padded by 16 bytes
-  static constexpr int PS = SS::DP + EPU;
+  // Column stride of the LDS state copy.  The bf16 TAYLOR2 copy is unpadded
+  // and swizzled instead (kStateSwizzle below); the others are padded by 16
+  // bytes.
+  static constexpr bool kStateSwizzle = MAP == MAP_TAYLOR2 && sizeof(T) == 2;
+  static constexpr int PS = kStateSwizzle ? SS::DP : SS::DP + EPU;
   static constexpr int KUR = DK / EPU;      // 16-byte units per k row
   static constexpr int VUR = DV / EPU;
   static constexpr int UK = C * DK / EPU;   // 16-byte units per k tile
