@@ -173,6 +173,21 @@ size_t slots_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nslot) {
   return (size_t)BH * (size_t)nslot * (size_t)slot_floats(map, dk, dv) * 4u;
 }
 
+// ELU1 without gates, default plan of two segments per head (128 to 255
+// heads): one launch in which segment 1's workgroup walks segment 0 first
+// without outputs (prefix_mode 3, as for the Taylor maps).
+// Such a chunk costs about kPreCost16 / 16 of a chunk with outputs (0.8
+// against 1.3 us measured), so segment 0 takes 1 / (2 - r) of the chunks,
+// rounded to whole two-chunk trips.
+constexpr int kPreCost16 = 8;
+
+int64_t elu1_seg0_chunks(int64_t nchunks) {
+  const double r = kPreCost16 / 16.0;
+  int64_t c0 = 2 * (int64_t)(nchunks / (2.0 - r) / 2.0 + 0.5);
+  if (c0 >= nchunks) c0 = (nchunks - 1) & ~(int64_t)1;
+  return c0 < 2 ? 2 : c0;
+}
+
 size_t workspace_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nseg,
                        int seg_chunks) {
   if (nseg <= 1) return 0;
@@ -361,6 +376,15 @@ linattn_status_t prefill_common(int map, int dtype, int64_t B, int64_t H,
     a.seg_chunks = (int)self_prefix_seg0_chunks(nchunks, dtype);
     a.sum_split = 1;
     a.ws_log = nullptr;
+  }
+  // ELU1 without gates at two segments per head, not in place (both
+  // workgroups of a head read the initial state, and segment 1's writes
+  // the final one): one launch as well.
+  if (prefill_map(map) == MAP_ELU1 && !gated && seg_len == 0 && nseg == 2 && !in_place &&
+      nchunks <= kMaxSegBytes / (kChunk * row_bytes)) {
+    a.prefix_mode = 3;
+    a.seg_chunks = (int)elu1_seg0_chunks(nchunks);
+    a.sum_split = 1;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = gated ? dispatch_prefill<true>(map, dtype, d_k, d_v, a, st)

@@ -35,9 +35,10 @@
 // state, seg_scan_kernel turns those sums into exclusive prefixes (plus the
 // optional initial state), and chunk_kernel<OUT = true> starts each segment
 // from its prefix.  With one segment per head only the last kernel runs.
-// The Taylor maps at two segments per head run one kernel instead
-// (chunk_kernel<..., PRE = true>): the workgroup of segment 1 walks segment
-// 0 first, advancing the state without outputs.
+// At two segments per head (the plain ELU1 map, and the Taylor maps plain
+// or gated) one kernel runs instead (chunk_kernel<..., PRE = true>): the
+// workgroup of segment 1 walks segment 0 first, advancing the state
+// without outputs.
 //
 // Feature order inside the kernels.  ELU1 uses the natural order.  TAYLOR2
 // (d_k = 16) keeps each unordered pair of key coordinates once: k_a k_b
@@ -505,8 +506,9 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// PRE: the prefix_mode 3 output kernel (TAYLOR2 only), a separate
-// instantiation so that the other plans keep their own compiled walk.
+// PRE: the prefix_mode 3 output kernel (TAYLOR2, and ELU1 without gates),
+// a separate instantiation so that the other plans keep their own compiled
+// walk.
 template <int MAP, typename T, int DK, int DV, bool OUT, bool GATED, bool PRE = false>
 __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void chunk_kernel(PrefillArgs a) {
   using SH = PrefillShape<MAP, T, DK, DV, kChunkWaves<MAP, T, DK, GATED, OUT>>;
@@ -590,13 +592,13 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void ch
   const int64_t N = a.N;
   int64_t tok_begin = (int64_t)seg * seg_chunks * C;
   int64_t tok_end = tok_begin + (int64_t)seg_chunks * C;
-  // TAYLOR2, prefix_mode 3 (two segments, no segment-sum pass; the PRE
-  // kernel): both workgroups of a head walk from token 0.  Segment 0 covers
+  // prefix_mode 3 (two segments, no segment-sum pass; the PRE kernel):
+  // both workgroups of a head walk from token 0.  Segment 0 covers
   // the first seg_chunks chunks; segment 1 walks those chunks first as a
   // pre-pass that only advances the state (chunks before c_out), then makes
   // the outputs of the rest of the sequence.
   constexpr bool kPrePass = PRE;
-  static_assert(!PRE || (OUT && MAP == MAP_TAYLOR2), "the pre-pass kernel");
+  static_assert(!PRE || (OUT && (MAP == MAP_TAYLOR2 || !GATED)), "the pre-pass kernels");
   int c_out = 0;
   if constexpr (kPrePass) {
     c_out = seg * seg_chunks;
@@ -749,7 +751,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   using SS = StateShape<MAP, DK, DV>;
   constexpr int NT = 64 * kChunkWaves<MAP, T, DK, GATED, true>;
   constexpr int NT_SUM = 64 * kChunkWaves<MAP, T, DK, GATED, false>;
-  if (a.nseg > 1 && a.prefix_mode != 3) {
+  if (a.nseg > 1 && a.prefix_mode < 3) {
     hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, false, GATED>),
                        dim3(a.BH * (a.nseg - 1) * a.sum_split), dim3(NT_SUM), 0, st, a);
     if (a.prefix_mode == 2) {
@@ -758,7 +760,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
                          st, a);
     }
   }
-  if constexpr (MAP == MAP_TAYLOR2) {
+  if constexpr (MAP == MAP_TAYLOR2 || !GATED) {
     if (a.prefix_mode == 3) {
       hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, true, GATED, true>),
                          dim3(a.BH * a.nseg), dim3(NT), 0, st, a);

@@ -37,7 +37,10 @@ struct PrefillArgs {
   int nseg;        // segments per (batch, head)
   int seg_chunks;  // chunks per segment
   int prefix_mode; // 0: one segment; 1: output workgroups add the preceding
-                   // segment sums themselves; 2: a scan kernel runs first
+                   // segment sums themselves; 2: a scan kernel runs first;
+                   // 3: two segments in one launch, segment 1's workgroup
+                   // walks segment 0 (seg_chunks chunks) first without
+                   // outputs
   int sum_split;   // the segment-sum pass splits each segment into this many
                    // equal parts (more, shorter workgroups when heads are few)
   int nslot;       // workspace slots per (batch, head): nseg * sum_split

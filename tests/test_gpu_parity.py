@@ -274,6 +274,64 @@ def test_prefill_two_segments_pre_pass(fmap, d_k, d_v, dtype, gated, with_state,
     assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
 
 
+# (B, H, N, d): ELU1 default plans.  At two segments per head (128 to 255
+# heads) one launch, in which segment 1's workgroup walks segment 0 first
+# (both workgroups of a head on one XCD when the heads fill groups of 8);
+# at 3 to 7 segments the segment-sum pass and direct prefixes.
+ELU1_PLAN_CASES = [(16, 8, 1100, 64),   # 2 segments, heads in groups of 8
+                   (3, 45, 1500, 32),   # 2 segments, 135 heads
+                   (9, 16, 1030, 16),   # 2 segments, ragged
+                   (5, 17, 1536, 32),   # 3 segments
+                   (4, 16, 2000, 64),   # 4 segments, ragged
+                   (2, 25, 2560, 16),   # 5 segments
+                   (6, 6, 3544, 32)]    # 7 segments, ragged
+
+
+@pytest.mark.parametrize("B,H,N,d", ELU1_PLAN_CASES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("state", ["zero", "given", "in_place"])
+def test_prefill_elu1_default_plans(B, H, N, d, dtype, state):
+    """The ELU1 default plans of 2 to 7 segments per head: every output row
+    and the exported state follow the recurrence, from zero, from an
+    arbitrary state, and in place (S_out = S_in, where the two-segment plan
+    takes the segment-sum pass and the scan instead), for both input
+    types."""
+    _log(f"elu1 default plan B={B} H={H} N={N} d={d} {dtype} state={state}")
+    q, k, v = synth.draw_qkv(B, H, N, d, d, seed=N + d, dtype=dtype)
+    S0 = z0 = None
+    Sd = zd = None
+    if state != "zero":
+        q0, k0, v0 = synth.draw_qkv(B, H, 90, d, d, seed=33, dtype="f32")
+        _, S_in, z_in = oracle.attention_recurrent(q0.f64(), k0.f64(), v0.f64(), "elu1")
+        S_in = S_in + np.random.default_rng(34).standard_normal(S_in.shape)
+        S32, z32 = S_in.astype(np.float32), z_in.astype(np.float32)
+        S0, z0 = S32.astype(np.float64), z32.astype(np.float64)
+        Sd, zd = torch.from_numpy(S32).to(DEV), torch.from_numpy(z32).to(DEV)
+    y_ref, S_ref, z_ref = oracle.attention_recurrent(q.f64(), k.f64(), v.f64(), "elu1",
+                                                     S0=S0, z0=z0)
+    L = ops.load_library()
+    dt = 0 if dtype == "f32" else 1
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    nws = ops.workspace_bytes("elu1", tdt, B, H, N, d, d, 0)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=DEV)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    y = torch.empty_like(vd)
+    if state == "in_place":
+        S, z = Sd, zd
+    else:
+        S = torch.empty((B, H, d, d), dtype=torch.float32, device=DEV)
+        z = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+    rc = L.linattn_prefill(0, dt, B, H, N, d, d, ops._ptr(qd), ops._ptr(kd), ops._ptr(vd),
+                           ops._ptr(y), ops._ptr(Sd), ops._ptr(zd), ops._ptr(S), ops._ptr(z),
+                           0, ops._ptr(ws), nws, ops._stream(qd))
+    assert rc == 0
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert row_err(ops.to_numpy64(y), y_ref) <= tol
+    assert state_err(ops.to_numpy64(S), S_ref) <= tol
+    assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
+
+
 @pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64)])
 def test_prefill_deterministic_and_segment_invariant(fmap, d_k, d_v):
     _log(f"determinism / segment invariance {fmap}")
@@ -389,14 +447,15 @@ def test_decode_graph_replays_match_eager(fmap, d_k, d_v):
 
 @pytest.mark.parametrize("case", ["one_segment", "part_sums", "scan", "taylor_state",
                                   "taylor_pre_pass", "gated_taylor_pre_pass", "gated",
-                                  "sliding_window"])
+                                  "elu1_pre_pass", "sliding_window"])
 def test_prefill_graph_replays_match_eager(case):
     """Prefill calls captured in one HIP graph: every replay (other eager work
     in between) gives bit-identical outputs and final states to the same
     calls run eagerly.  The cases cover one segment per head, output
     workgroups adding their predecessors' part sums, the scan kernel, the
     Taylor state export, the Taylor two-segment plan without a segment-sum
-    pass (plain and gated), the gated form, and the sliding-window prefill
+    pass (plain and gated), the same plan for ELU1, the gated form, and the
+    sliding-window prefill
     with a generation step (its caches restored by an eager copy before
     each replay)."""
     _log(f"prefill graph replays {case}")
@@ -407,6 +466,7 @@ def test_prefill_graph_replays_match_eager(case):
                               "taylor_pre_pass": ("taylor2", 16, 64, 1024, 0),
                               "gated_taylor_pre_pass": ("taylor2", 16, 64, 1024, 0),
                               "gated": ("elu1", 64, 64, 1000, 64),
+                              "elu1_pre_pass": ("elu1", 64, 64, 1100, 0),
                               "sliding_window": ("elu1", 64, 64, 700, 0)}[case]
     q, k, v = synth.draw_qkv(2, 3, N, d_k, d_v, seed=41, dtype="bf16", qk_scale=_qk_scale(fmap))
     qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
