@@ -5,6 +5,7 @@
 // HIP call, so an invalid call neither launches nor writes anything and
 // makes no HIP runtime call at all.
 #include <limits.h>
+#include <math.h>
 #include <stdint.h>
 
 #include <mutex>
@@ -434,6 +435,10 @@ linattn_status_t decode_common(int map, int dtype, int64_t B, int64_t H,
 
 bool swa_dim_ok(int64_t d) { return d == 32 || d == 64 || d == 128; }
 
+// The usual softmax scale, 1/sqrt(d), taken when the caller passes NaN
+// (d <= 0 gives NaN, which validation rejects with d).
+float default_swa_scale(int64_t d) { return d > 0 ? (float)(1.0 / sqrt((double)d)) : NAN; }
+
 hipError_t dispatch_swa_prefill(int dtype, int64_t d, const void* q, const void* k,
                                 const void* v, void* y, void* kc, void* vc, int64_t BH,
                                 int64_t N, int64_t window, float scale, hipStream_t st) {
@@ -598,6 +603,7 @@ linattn_status_t linattn_swa_prefill(int dtype, int64_t B, int64_t H, int64_t N,
                                      const void* q, const void* k, const void* v,
                                      void* y, void* k_cache, void* v_cache,
                                      void* stream) {
+  if (scale != scale) scale = default_swa_scale(d);
   if (!valid_dtype(dtype) || B <= 0 || H <= 0 || N <= 0 || d <= 0 || window <= 0 ||
       !finite(scale))
     return LINATTN_ERR_INVALID_ARGUMENT;
@@ -638,6 +644,7 @@ linattn_status_t linattn_swa_decode_step(int dtype, int64_t B, int64_t H, int64_
                                          const void* k, const void* v, const int64_t* pos,
                                          void* k_cache, void* v_cache, void* y,
                                          void* stream) {
+  if (scale != scale) scale = default_swa_scale(d);
   if (!valid_dtype(dtype) || B <= 0 || H <= 0 || d <= 0 || window <= 0 || !finite(scale))
     return LINATTN_ERR_INVALID_ARGUMENT;
   if (!swa_dim_ok(d) || window > kSwaMaxWindow) return LINATTN_ERR_UNSUPPORTED;

@@ -311,14 +311,14 @@ def _decode(q, k, v, gate, normalize, S, z, fmap, out):
 def swa_prefill(q, k, v, window: int, *, scale=None, return_cache=False, out=None):
     """Sliding-window softmax attention over [B, H, N, d] inputs.
 
-    scale defaults to 1/sqrt(d).  return_cache: also return the ring caches
+    scale defaults to 1/sqrt(d) (the library's choice, passed as NaN).  return_cache: also return the ring caches
     (k_cache, v_cache) [B, H, window, d] for swa_decode_step."""
     L = load_library()
     _qkv(q, k, v, 4)
     if v.shape != q.shape:
         raise ValueError("expected q, k, v [B,H,N,d] of one shape")
     B, H, N, d = q.shape
-    sc = float(d) ** -0.5 if scale is None else float(scale)
+    sc = float("nan") if scale is None else float(scale)  # NaN: the library's 1/sqrt(d)
     if out is not None:
         _expect("out", out, v.shape, v.dtype)
     _need_cuda(q, k, v, out)
@@ -348,7 +348,7 @@ def swa_decode_step(q, k, v, pos, k_cache, v_cache, window: int, *, scale=None, 
     if out is not None:
         _expect("out", out, v.shape, v.dtype)
     _need_cuda(q, k, v, pos, k_cache, v_cache, out)
-    sc = float(d) ** -0.5 if scale is None else float(scale)
+    sc = float("nan") if scale is None else float(scale)  # NaN: the library's 1/sqrt(d)
     y = out if out is not None else torch.empty_like(v)
     _check(L.linattn_swa_decode_step(_dtype_id(q), B, H, d, window, sc, _ptr(q), _ptr(k),
                                      _ptr(v), _ptr(pos), _ptr(k_cache), _ptr(v_cache),

@@ -86,6 +86,11 @@ typedef enum linattn_dtype {
   LINATTN_DTYPE_BF16 = 1
 } linattn_dtype_t;
 
+/* Every entry point takes its map and dtype codes (the values above) as
+   plain int, so that any value a caller passes reaches validation and an
+   unknown code returns LINATTN_ERR_INVALID_ARGUMENT rather than being an
+   out-of-range enum inside the library. */
+
 /* Static text for a status code (never NULL). */
 const char* linattn_status_string(int status);
 
@@ -259,7 +264,7 @@ linattn_status_t linattn_decode_step_gated(int map, int dtype, int64_t B, int64_
  *     y_i  = sum_j p_ij v_j.
  *   q, k, v, y  [B, H, N, d] of `dtype` (d_k = d_v = d); d in {32, 64, 128}.
  *   window      w >= 1 (w >= N is causal softmax attention).
- *   scale       any finite float; 1/sqrt(d) is the usual choice.
+ *   scale       any finite float, or NaN for the usual 1/sqrt(d).
  *   k_cache, v_cache  [B, H, w, d] of `dtype`, or both NULL: when given,
  *               they receive the ring cache that linattn_swa_decode_step
  *               continues from -- token t (t >= N - w) in slot t mod w,
@@ -288,6 +293,7 @@ linattn_status_t linattn_swa_prefill(int dtype, int64_t B, int64_t H, int64_t N,
  *   k_cache, v_cache  [B, H, w, d] of `dtype`, updated in place; slots not
  *               yet reached are never read.
  *   window      1 <= w <= 4096 (else LINATTN_ERR_UNSUPPORTED).
+ *   scale       as for linattn_swa_prefill (NaN: 1/sqrt(d)).
  * All arithmetic is float32; y is rounded to dtype.
  */
 linattn_status_t linattn_swa_decode_step(int dtype, int64_t B, int64_t H, int64_t d,

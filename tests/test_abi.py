@@ -220,8 +220,11 @@ def test_swa_validation_codes(lib):
     assert pre(q=None) == INV
     assert pre(N=0) == INV
     assert pre(w=0) == INV
-    assert pre(scale=float("nan")) == INV
     assert pre(scale=float("inf")) == INV
+    # NaN selects 1/sqrt(d): it passes the scale check, so the unsupported
+    # width is what the call reports (no launch either way)
+    assert pre(scale=float("nan"), d=48) == UNS
+    assert pre(scale=float("-inf"), d=48) == INV
     assert pre(d=48) == UNS
     assert pre(dtype=7) == INV
     assert pre(kc=A["Si"]) == INV                     # v_cache missing
@@ -241,6 +244,8 @@ def test_swa_validation_codes(lib):
     assert dec(kc=None) == INV
     assert dec(w=4097) == UNS                         # beyond the generation window
     assert dec(d=16) == UNS
+    assert dec(d=16, scale=float("nan")) == UNS
+    assert dec(d=16, scale=float("inf")) == INV
     assert dec(pos=ctypes.c_void_p(0x60000004)) == INV  # pos not 8-byte aligned
     assert dec(y=A["Si"]) == INV                      # y aliases the key cache
     assert dec(kc=A["q"]) == INV                      # cache aliases an input

@@ -814,6 +814,31 @@ def test_swa_prefill_small(d, dtype, N, w):
     assert np.array_equal(ops.to_numpy64(vc), vc_ref)
 
 
+def test_swa_default_scale_is_one_over_sqrt_d():
+    """The sliding-window entry points take NaN for their default softmax
+    scale 1/sqrt(d): bit-identical to passing that scale, and an explicit
+    scale is honoured (checked against the oracle at scale 0.3)."""
+    _log("swa default scale")
+    d, w, N = 64, 48, 300
+    q, k, v = synth.draw_qkv(2, 3, N, d, d, seed=77, dtype="bf16")
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    y0 = ops.swa_prefill(qd, kd, vd, w)
+    y1 = ops.swa_prefill(qd, kd, vd, w, scale=d ** -0.5)
+    y2 = ops.swa_prefill(qd, kd, vd, w, scale=0.3)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    assert row_err(ops.to_numpy64(y2), oracle.swa_attention(q.f64(), k.f64(), v.f64(), w, 0.3)) <= TOL["bf16"]
+    _, (kc, vc) = ops.swa_prefill(qd, kd, vd, w, return_cache=True)
+    qs, ks, vs = (ops.to_device(x, DEV)[:, :, 0].contiguous()
+                  for x in synth.draw_qkv(2, 3, 1, d, d, seed=78, dtype="bf16", stream=1))
+    pos = torch.full((2,), N, dtype=torch.int64, device=DEV)
+    kc2, vc2 = kc.clone(), vc.clone()
+    z0 = ops.swa_decode_step(qs, ks, vs, pos, kc, vc, w)
+    z1 = ops.swa_decode_step(qs, ks, vs, pos, kc2, vc2, w, scale=d ** -0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(z0, z1)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("w", [64, 100])
 def test_swa_prefill_long_runs(dtype, w):
