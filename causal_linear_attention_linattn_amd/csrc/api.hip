@@ -174,12 +174,14 @@ size_t slots_bytes(int map, int64_t BH, int64_t dk, int64_t dv, int nslot) {
   return (size_t)BH * (size_t)nslot * (size_t)slot_floats(map, dk, dv) * 4u;
 }
 
-// ELU1 without gates, default plan of two segments per head (128 to 255
-// heads): one launch in which segment 1's workgroup walks segment 0 first
-// without outputs (prefix_mode 3, as for the Taylor maps).
-// Such a chunk costs about kPreCost16 / 16 of a chunk with outputs (0.8
-// against 1.3 us measured), so segment 0 takes 1 / (2 - r) of the chunks,
-// rounded to whole two-chunk trips.
+// ELU1, default plan of two segments per head (128 to 255 heads): one
+// launch in which segment 1's workgroup walks segment 0 first without
+// outputs (prefix_mode 3, as for the Taylor maps).  Segment 0 takes
+// 1 / (2 - r) of the chunks, rounded to whole two-chunk trips, where r
+// stands for the cost of a chunk walked without outputs against one with
+// them: measured best at 8/16 for the plain map (B=16 H=8 N=2048..4096,
+// 6 to 12/16 tried; such a chunk takes ~0.8 us against ~1.3 us) and for
+// the gated map (6 to 12/16 tried at B=16 H=8 N=2048..4096).
 constexpr int kPreCost16 = 8;
 
 int64_t elu1_seg0_chunks(int64_t nchunks) {
@@ -378,14 +380,20 @@ linattn_status_t prefill_common(int map, int dtype, int64_t B, int64_t H,
     a.sum_split = 1;
     a.ws_log = nullptr;
   }
-  // ELU1 without gates at two segments per head, not in place (both
-  // workgroups of a head read the initial state, and segment 1's writes
-  // the final one): one launch as well.
-  if (prefill_map(map) == MAP_ELU1 && !gated && seg_len == 0 && nseg == 2 && !in_place &&
+  // ELU1 at two segments per head, not in place (both workgroups of a head
+  // read the initial state, and segment 1's writes the final one): one
+  // launch as well.  The gated kernel holds one workgroup per compute unit,
+  // and past 128 heads its late workgroups, which walk the whole sequence,
+  // start only when early ones end: measured on one MI355X at B=20 H=8
+  // N=3000 d=64 bf16, 127.3 us with the segment-sum plan against 134.8 us;
+  // at B=16 H=8 N=4096, 100.4 against 90.8 us.
+  if (prefill_map(map) == MAP_ELU1 && seg_len == 0 && nseg == 2 && !in_place &&
+      (!gated || BH * 2 <= kTargetWorkgroups) &&
       nchunks <= kMaxSegBytes / (kChunk * row_bytes)) {
     a.prefix_mode = 3;
     a.seg_chunks = (int)elu1_seg0_chunks(nchunks);
     a.sum_split = 1;
+    a.ws_log = nullptr;
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = gated ? dispatch_prefill<true>(map, dtype, d_k, d_v, a, st)

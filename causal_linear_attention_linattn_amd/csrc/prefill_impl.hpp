@@ -35,8 +35,8 @@
 // state, seg_scan_kernel turns those sums into exclusive prefixes (plus the
 // optional initial state), and chunk_kernel<OUT = true> starts each segment
 // from its prefix.  With one segment per head only the last kernel runs.
-// At two segments per head (the plain ELU1 map, and the Taylor maps plain
-// or gated) one kernel runs instead (chunk_kernel<..., PRE = true>): the
+// At two segments per head (every map, plain or gated) one kernel runs
+// instead (chunk_kernel<..., PRE = true>): the
 // workgroup of segment 1 walks segment 0 first, advancing the state
 // without outputs.
 //
@@ -506,9 +506,8 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// PRE: the prefix_mode 3 output kernel (TAYLOR2, and ELU1 without gates),
-// a separate instantiation so that the other plans keep their own compiled
-// walk.
+// PRE: the prefix_mode 3 output kernel, a separate instantiation so that
+// the other plans keep their own compiled walk.
 template <int MAP, typename T, int DK, int DV, bool OUT, bool GATED, bool PRE = false>
 __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void chunk_kernel(PrefillArgs a) {
   using SH = PrefillShape<MAP, T, DK, DV, kChunkWaves<MAP, T, DK, GATED, OUT>>;
@@ -598,7 +597,7 @@ __global__ __launch_bounds__((64 * kChunkWaves<MAP, T, DK, GATED, OUT>)) void ch
   // pre-pass that only advances the state (chunks before c_out), then makes
   // the outputs of the rest of the sequence.
   constexpr bool kPrePass = PRE;
-  static_assert(!PRE || (OUT && (MAP == MAP_TAYLOR2 || !GATED)), "the pre-pass kernels");
+  static_assert(!PRE || OUT, "the pre-pass kernels");
   int c_out = 0;
   if constexpr (kPrePass) {
     c_out = seg * seg_chunks;
@@ -760,12 +759,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
                          st, a);
     }
   }
-  if constexpr (MAP == MAP_TAYLOR2 || !GATED) {
-    if (a.prefix_mode == 3) {
-      hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, true, GATED, true>),
-                         dim3(a.BH * a.nseg), dim3(NT), 0, st, a);
-      return hipGetLastError();
-    }
+  if (a.prefix_mode == 3) {
+    hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, true, GATED, true>),
+                       dim3(a.BH * a.nseg), dim3(NT), 0, st, a);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((chunk_kernel<MAP, T, DK, DV, true, GATED>),
                      dim3(a.BH * a.nseg), dim3(NT), 0, st, a);

@@ -332,6 +332,37 @@ def test_prefill_elu1_default_plans(B, H, N, d, dtype, state):
     assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
 
 
+@pytest.mark.parametrize("B,H,N,d", [(16, 8, 1100, 64), (4, 32, 1500, 32), (8, 16, 1030, 16),
+                                     (3, 45, 1500, 32)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_prefill_gated_elu1_two_segments(B, H, N, d, dtype, with_state):
+    """Gated ELU1 at two default segments per head: at 128 heads the
+    one-launch pre-pass plan (segment 1's workgroup decays and advances the
+    state over segment 0 without outputs), past 128 heads the segment-sum
+    plan.  Outputs and the exported state follow the gated recurrence, from
+    zero or from an arbitrary state, with resets in the coefficients."""
+    _log(f"gated elu1 two segments B={B} H={H} N={N} d={d} {dtype} state={with_state}")
+    q, k, v = synth.draw_qkv(B, H, N, d, d, seed=N + 3 * d, dtype=dtype)
+    a = synth.draw_gate(B, H, N, seed=N + 1, lo=0.97, reset_p=0.002)
+    S0 = z0 = st = None
+    if with_state:
+        q0, k0, v0 = synth.draw_qkv(B, H, 90, d, d, seed=35, dtype="f32")
+        _, S_in, z_in = oracle.attention_recurrent(q0.f64(), k0.f64(), v0.f64(), "elu1")
+        S32, z32 = S_in.astype(np.float32), z_in.astype(np.float32)
+        S0, z0 = S32.astype(np.float64), z32.astype(np.float64)
+        st = (torch.from_numpy(S32).to(DEV), torch.from_numpy(z32).to(DEV))
+    y_ref, S_ref, z_ref = oracle.attention_gated_recurrent(
+        q.f64(), k.f64(), v.f64(), a.astype(np.float64), "elu1", S0=S0, z0=z0)
+    qd, kd, vd = (ops.to_device(x, DEV) for x in (q, k, v))
+    y, (S, z) = ops.prefill_gated(qd, kd, vd, _gate_dev(a), "elu1", state=st, return_state=True)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert row_err(ops.to_numpy64(y), y_ref) <= tol
+    assert state_err(ops.to_numpy64(S), S_ref) <= tol
+    assert state_err(ops.to_numpy64(z)[..., None], z_ref[..., None]) <= tol
+
+
 @pytest.mark.parametrize("fmap,d_k,d_v", [("elu1", 64, 64), ("taylor2", 16, 64)])
 def test_prefill_deterministic_and_segment_invariant(fmap, d_k, d_v):
     _log(f"determinism / segment invariance {fmap}")
