@@ -370,6 +370,10 @@ DIGEST_FILES = {
                       "chunk_walk.inc", "prefill_elu1_bf16_gated.hip"),
     "swa_prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp", "swa.hip"),
     "swa_decode": ("api.hip", "device.hpp", "shapes.hpp", "swa.hip"),
+    "long_prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp", "chunk_walk.inc",
+                     "prefill_elu1_bf16.hip"),
+    "gated_taylor2_prefill": ("api.hip", "device.hpp", "shapes.hpp", "prefill_impl.hpp",
+                              "chunk_walk.inc", "prefill_taylor2_bf16_gated.hip"),
 }
 
 
@@ -616,7 +620,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy used to scale HBM counters")
     ap.add_argument("--only", choices=("taylor2_prefill", "gated_prefill", "swa_prefill",
-                                       "swa_decode"),
+                                       "swa_decode", "long_prefill", "gated_taylor2_prefill"),
                     help="time one secondary section alone and print its record "
                          "(for per-kernel profiles of that section)")
     args = ap.parse_args()
@@ -660,6 +664,13 @@ def main():
         elif args.only == "gated_prefill":
             c, m_, _ = time_prefill(args, ops, synth, torch, gated=True)
             rec = prefill_record(c, m_)
+        elif args.only == "long_prefill":
+            c, m_, _ = time_prefill(args, ops, synth, torch, name="long_elu1_bf16")
+            rec = prefill_record(c, m_)
+        elif args.only == "gated_taylor2_prefill":
+            c, m_, _ = time_prefill(args, ops, synth, torch, name="based_taylor2_bf16",
+                                    gated=True)
+            rec = prefill_record(c, m_)
         elif args.only == "swa_prefill":
             rec = time_swa_prefill(args, ops, synth, torch)
         else:
@@ -685,6 +696,7 @@ def main():
                                           f"N={c2['N']} d_k={c2['d_k']} d_v={c2['d_v']} "
                                           f"{c2['dtype']}"))
         others["based_taylor2_bf16"]["traffic"] = recorded_traffic("taylor2_prefill")
+        others["long_elu1_bf16"]["traffic"] = recorded_traffic("long_prefill")
         # linear in N: ELU1 bf16, B=1 H=8 d=64, N from 4K to 64K
         sweep = []
         for n in (4096, 8192, 16384, 32768, 65536):
@@ -704,6 +716,7 @@ def main():
                           f"B={c4['B']} H={c4['H']} N={c4['N']} d_k={c4['d_k']} "
                           f"d_v={c4['d_v']} {c4['dtype']}"))
         others["gated_" + PREFILL]["traffic"] = recorded_traffic("gated_prefill")
+        others["gated_based_taylor2_bf16"]["traffic"] = recorded_traffic("gated_taylor2_prefill")
     decode_rec = None
     if not args.no_decode:
         dcfg, dms, finite, dms_graph = time_decode(args, ops, synth, torch)
