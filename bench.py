@@ -419,6 +419,75 @@ def recorded_traffic(kind):
     return None
 
 
+def achievable_peaks(torch):
+    """What this device reaches, beside the published peaks: three plain
+    1 GiB streams of 16-byte vectors, contiguous ranges per workgroup, best
+    of twelve launch shapes each (4, 8 or 16 vectors in flight per thread;
+    1024 to 8192 workgroups) (a copy into a second buffer, a read-only pass,
+    and an in-place read-and-write pass; bytes moved / time), and a loop of
+    independent bf16 16x16x32 MFMAs on registers, at one and two waves per
+    SIMD (all in liblinattn_probe.so)."""
+    import ctypes
+
+    out = {}
+    path = os.path.join(ROOT, "causal_linear_attention_linattn_amd", "liblinattn_probe.so")
+    if not os.path.exists(path):
+        return None
+    P = ctypes.CDLL(path)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    P.linattn_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for mode, name, moved in ((0, "copy", 2 * n), (1, "read", n), (2, "read_write_in_place", 2 * n)):
+        best, shape = 0.0, None
+        for depth in (4, 8, 16):
+            for wgs in (1024, 2048, 4096, 8192):
+                args = (mode, depth, ctypes.c_void_p(src.data_ptr()),
+                        ctypes.c_void_p(dst.data_ptr()), n, wgs, st)
+                for _ in range(2):
+                    if P.linattn_probe_stream(*args):
+                        raise RuntimeError("stream probe launch failed")
+                reps = 8
+                ev0.record()
+                for _ in range(reps):
+                    P.linattn_probe_stream(*args)
+                ev1.record()
+                torch.cuda.synchronize()
+                rate = moved * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+                if rate > best:
+                    best, shape = rate, f"{depth} vectors in flight per thread, {wgs} workgroups"
+        out[f"hbm_{name}_GBs"] = best
+        out[f"hbm_{name}_best_shape"] = shape
+    out["hbm_best_frac_of_published"] = max(
+        v for k, v in out.items() if k.endswith("_GBs")) / HBM_PEAK_GBS
+    del src, dst
+    P.linattn_probe_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    iters = 20000
+    for per_simd in (1, 2):
+        wgs = 256 * per_simd
+        sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        args = (iters, wgs, ctypes.c_void_p(sink.data_ptr()), st)
+        if P.linattn_probe_peak_mfma(*args):
+            raise RuntimeError("MFMA loop launch failed")
+        ev0.record()
+        P.linattn_probe_peak_mfma(*args)
+        ev1.record()
+        torch.cuda.synchronize()
+        flops = wgs * 4 * iters * 8 * 2 * 16 * 16 * 32
+        tf = flops / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
+        out[f"mfma_bf16_loop_TFLOPs_{per_simd}wave_per_simd"] = tf
+    best = max(v for k, v in out.items() if k.startswith("mfma_bf16_loop"))
+    out["mfma_bf16_loop_frac_of_published"] = best / MFMA_BF16_PEAK_TFLOPS
+    return out
+
+
 def copy_calibration(torch):
     """A plain device copy of known size (256 MiB read + 256 MiB written),
     run under rocprofv3 --pmc to scale FETCH_SIZE / WRITE_SIZE to bytes."""
@@ -761,6 +830,7 @@ def main():
                 "graph_ms_per_step": gms_graph,
             }
     probe = intra_mfma_probe(torch) if not args.no_other_configs else None
+    peaks = achievable_peaks(torch) if not args.no_other_configs else None
 
     cfg, ms, nsets = time_prefill(args, ops, synth, torch, prepared=headline)
     del headline
@@ -787,6 +857,7 @@ def main():
             "global_batch": cfg["B"], "seq_len": cfg["N"], "heads": cfg["H"],
             "d_k": cfg["d_k"], "d_v": cfg["d_v"], "feature_map": cfg["fmap"],
             "parallelism": "single-gpu", "input_sets_rotated": nsets,
+            "seed": 0,
         },
         "roofline": {
             "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -802,6 +873,9 @@ def main():
         out["other_configs"] = others
     if probe:
         out["roofline"]["intra_chunk_mfma_probe"] = probe
+    if peaks:
+        peaks["headline_frac_of_read_rate"] = gbs / peaks["hbm_read_GBs"]
+        out["roofline"]["achievable_on_device"] = peaks
     if decode_rec is not None:
         out["decode"] = decode_rec
     if cpu_prefill is not None:
