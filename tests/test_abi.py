@@ -355,3 +355,36 @@ def test_noalloc_rejects_calls_beyond_its_fixed_scratch(lib):
     # argument errors still come first
     assert lib.linattn_prefill_noalloc(1, 1, 8, 16, 8192, 16, 64, None, A["k"], A["v"],
                                        A["y"], None, None, None, None, 64, None) == 1
+
+
+def test_probe_library_exports_what_bench_calls():
+    """liblinattn_probe.so exports every probe entry point bench.py calls,
+    and its argument checks reject bad calls on the host, before any launch."""
+    from causal_linear_attention_linattn_amd import _build
+    if not os.path.exists(_build.PROBE_LIB):
+        _build.build()
+    P = ctypes.CDLL(_build.PROBE_LIB)
+    used = set(re.findall(r"\bP\.(linattn_probe_[a-z_0-9]+)",
+                          open(os.path.join(ROOT, "bench.py")).read()))
+    assert {"linattn_probe_stream", "linattn_probe_peak_mfma",
+            "linattn_probe_intra_mfma"} <= used
+    for name in used:
+        assert hasattr(P, name), name
+    P.linattn_probe_intra_mfma_per_iter.argtypes = [ctypes.c_int]
+    assert P.linattn_probe_intra_mfma_per_iter(0) > 0
+    assert P.linattn_probe_intra_mfma_per_iter(1) > 0
+    assert P.linattn_probe_intra_mfma_per_iter(2) == -1
+    st = P.linattn_probe_stream
+    st.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below is rejected
+    assert st(0, 4, None, fake, 1 << 20, 16, None) == 1        # no source
+    assert st(0, 4, fake, fake, (1 << 20) + 8, 16, None) == 1  # not whole 16-byte vectors
+    assert st(0, 4, fake, fake, 1 << 20, 0, None) == 1         # no workgroups
+    assert st(0, 4, fake, fake, 1 << 12, 2, None) == 1         # under 4 KB per workgroup
+    assert st(0, 5, fake, fake, 1 << 20, 16, None) == 1        # unsupported depth
+    assert st(3, 4, fake, fake, 1 << 20, 16, None) == 1        # unknown mode
+    pk = P.linattn_probe_peak_mfma
+    pk.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert pk(0, 256, fake, None) == 1
+    assert pk(10, 256, None, None) == 1
