@@ -980,9 +980,10 @@ def _default_segments(BH, N):
 def test_full_size_prefill(name, rows_per_head):
     """Full-size workloads in the default launch configuration.  Every
     (b, h) is checked against the definition on t = 0, t = N - 1, the first
-    and last row of every segment of the default plan and random rows
-    (rows_per_head in all, at least); the final state of every head against
-    its closed form; every row against the convex hull."""
+    and last row of every segment of the default plan (up to N = 4096: of
+    every chunk) and random rows (rows_per_head in all, at least); the final
+    state of every head against its closed form; every row against the
+    convex hull."""
     _log(f"full-size prefill {name}")
     cfg = synth.WORKLOADS[name]
     fmap = cfg["fmap"]
@@ -999,7 +1000,13 @@ def test_full_size_prefill(name, rows_per_head):
     assert np.all(y >= lo - slack) and np.all(y <= hi + slack)
     del lo, hi, slack
     seg = _default_segments(B * H, N)
-    ends = sorted({0, N - 1} | _segment_ends(0, N, seg))
+    ends = {0, N - 1} | _segment_ends(0, N, seg)
+    if N <= 4096:
+        # both rows at every chunk boundary: whatever segment lengths the
+        # plan picks (the two-segment plans split unevenly), each segment's
+        # first and last rows are among them
+        ends |= {t for c in range(1, -(-N // 64)) for t in (64 * c - 1, 64 * c)}
+    ends = sorted(ends)
     rng = np.random.default_rng(1)
     q64, k64 = q.f64(), k.f64()
     for b in range(B):
